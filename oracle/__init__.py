@@ -1,0 +1,199 @@
+"""CPU oracle for the MoE dispatch/combine path (ctypes over ``moe_ref.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the library or its binding.  It shares
+no code with the HIP path; both are fed from ``moe_inputs``.
+
+Each function follows the definition stated in ``moe_ref.c`` (gate:
+"Efficient and portable mixture-of-experts communication", Introduction;
+layout: the same page's "Dispatch" section, Cobalt Section 1 for node-level
+deduplication and the OCS decode paper's "Variable MoE Traffic and
+Regularization" for per-destination row counts; pack and combine: the same
+blog's "Dispatch" and "Combine" sections).  All are pinned by the CPU tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+_LIB: Optional[ctypes.CDLL] = None
+
+DT_F32 = 0
+DT_BF16 = 1
+
+_P = ctypes.c_void_p
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        lib.moe_ref_gate.argtypes = [ctypes.c_int] * 4 + [_P, _P, _P]
+        lib.moe_ref_layout.argtypes = [ctypes.c_int] * 5 + [_P] * 12
+        lib.moe_ref_pack.argtypes = [ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_size_t, _P, _P, _P]
+        lib.moe_ref_combine.argtypes = ([ctypes.c_int] * 4 + [_P] * 5 +
+                                        [ctypes.c_int, _P, _P])
+        lib.moe_ref_combine_tokens.argtypes = (
+            [ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int] +
+            [_P] * 6)
+        lib.moe_ref_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.moe_ref_f64_to_bf16.restype = ctypes.c_uint16
+        for f in ("moe_ref_gate", "moe_ref_layout", "moe_ref_pack",
+                  "moe_ref_combine", "moe_ref_combine_tokens"):
+            getattr(lib, f).restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its input (code {rc})")
+
+
+def gate(logits: np.ndarray, K: int, renorm: bool = True):
+    """Top-K experts per token and their gate weights.
+
+    Returns ``(topk_idx int32 [T,K], topk_w fp32 [T,K])``.
+    """
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, K), dtype=np.int32)
+    w = np.empty((T, K), dtype=np.float32)
+    _check(_lib().moe_ref_gate(T, E, K, int(bool(renorm)), _ptr(logits),
+                               _ptr(idx), _ptr(w)), "gate")
+    return idx, w
+
+
+def layout(topk_idx: np.ndarray, E: int, R: int, N: int,
+           with_node_slot: bool = True) -> dict:
+    """Dispatch layout of ``topk_idx`` (int32 [T,K]); see ``moe_ref.c``."""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, K = topk_idx.shape
+    o = {
+        "expert_count": np.empty(E, np.int32),
+        "expert_off": np.empty(E + 1, np.int32),
+        "rank_count": np.empty(R, np.int32),
+        "rank_off": np.empty(R + 1, np.int32),
+        "rank_token_count": np.empty(R, np.int32),
+        "node_mask": np.empty(T, np.uint64),
+        "node_count": np.empty(N, np.int32),
+        "node_off": np.empty(N + 1, np.int32),
+        "node_slot": np.empty((T, N), np.int32) if with_node_slot else None,
+        "slot_pos": np.empty((T, K), np.int32),
+        "row_src": np.empty(T * K, np.int32),
+    }
+    _check(_lib().moe_ref_layout(
+        T, E, K, R, N, _ptr(topk_idx), _ptr(o["expert_count"]),
+        _ptr(o["expert_off"]), _ptr(o["rank_count"]), _ptr(o["rank_off"]),
+        _ptr(o["rank_token_count"]), _ptr(o["node_mask"]),
+        _ptr(o["node_count"]), _ptr(o["node_off"]), _ptr(o["node_slot"]),
+        _ptr(o["slot_pos"]), _ptr(o["row_src"])), "layout")
+    if not with_node_slot:
+        del o["node_slot"]
+    return o
+
+
+def pack(x: np.ndarray, slot_pos: np.ndarray) -> np.ndarray:
+    """``send[slot_pos[t,k]] = x[t]`` bit for bit; returns send [T*K, H]."""
+    x = np.ascontiguousarray(x)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    T, K = slot_pos.shape
+    assert x.shape[0] == T
+    send = np.empty((T * K,) + x.shape[1:], dtype=x.dtype)
+    row_bytes = x[0].nbytes if T > 0 else 0
+    _check(_lib().moe_ref_pack(T, K, row_bytes, _ptr(x), _ptr(slot_pos),
+                               _ptr(send)), "pack")
+    return send
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.uint16:
+        return DT_BF16
+    raise TypeError(f"rows must be fp32 or bf16 bits (uint16), got {a.dtype}")
+
+
+def combine(y: np.ndarray, slot_pos: np.ndarray, topk_w: np.ndarray,
+            topk_idx: Optional[np.ndarray] = None,
+            expert_scale: Optional[np.ndarray] = None,
+            out_dtype: str = "bf16"):
+    """Gate-weighted sum of each token's K expert rows.
+
+    Returns ``(out, exact)``: ``out`` rounded to nearest-even in ``out_dtype``
+    (fp32, or bf16 bits as uint16) and ``exact`` the unrounded fp64 sums.
+    """
+    y = np.ascontiguousarray(y)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    T, K = slot_pos.shape
+    H = y.shape[1]
+    if expert_scale is not None:
+        expert_scale = np.ascontiguousarray(expert_scale, dtype=np.float32)
+        topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    ocode = DT_F32 if out_dtype == "f32" else DT_BF16
+    out = np.empty((T, H), np.float32 if ocode == DT_F32 else np.uint16)
+    exact = np.empty((T, H), np.float64)
+    _check(_lib().moe_ref_combine(
+        T, H, K, _dtype_code(y), _ptr(y), _ptr(slot_pos), _ptr(topk_w),
+        _ptr(topk_idx), _ptr(expert_scale), ocode, _ptr(out), _ptr(exact)),
+        "combine")
+    return out, exact
+
+
+def combine_tokens(tokens: np.ndarray, y: np.ndarray, slot_pos: np.ndarray,
+                   topk_w: np.ndarray, topk_idx: Optional[np.ndarray] = None,
+                   expert_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Unrounded fp64 combine of the listed tokens only ([len(tokens), H])."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    y = np.ascontiguousarray(y)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    K = slot_pos.shape[1]
+    H = y.shape[1]
+    if expert_scale is not None:
+        expert_scale = np.ascontiguousarray(expert_scale, dtype=np.float32)
+        topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    exact = np.empty((len(tokens), H), np.float64)
+    _check(_lib().moe_ref_combine_tokens(
+        len(tokens), _ptr(tokens), H, K, _dtype_code(y), _ptr(y),
+        _ptr(slot_pos), _ptr(topk_w), _ptr(topk_idx), _ptr(expert_scale),
+        _ptr(exact)), "combine_tokens")
+    return exact
+
+
+def f64_to_bf16(values) -> np.ndarray:
+    """Round fp64 values to bf16 (nearest, ties to even); uint16 bits."""
+    v = np.asarray(values, dtype=np.float64).ravel()
+    f = _lib().moe_ref_f64_to_bf16
+    return np.array([f(float(a)) for a in v], dtype=np.uint16)
+
+
+def dispatch_combine(x: np.ndarray, logits: np.ndarray, K: int, R: int,
+                     N: int, expert_scale: Optional[np.ndarray] = None,
+                     out_dtype: str = "bf16", renorm: bool = True) -> dict:
+    """The whole path: gate -> layout -> pack -> combine with Y = send."""
+    idx, w = gate(logits, K, renorm)
+    E = logits.shape[1]
+    lay = layout(idx, E, R, N)
+    send = pack(x, lay["slot_pos"])
+    out, exact = combine(send, lay["slot_pos"], w, idx, expert_scale,
+                         out_dtype)
+    res = dict(lay)
+    res.update(topk_idx=idx, topk_w=w, send=send, out=out, out_exact=exact)
+    return res

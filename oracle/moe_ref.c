@@ -1,0 +1,339 @@
+/*
+ * moe_ref.c -- CPU oracle for MoE top-K gating, dispatch layout, dispatch
+ * packing and the gate-weighted combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, single-threaded
+ * statement of what the path computes.  Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg may build, load or call it.  It shares no
+ * code, header, table or helper with the HIP library, and includes nothing
+ * from it.  Floating point that produces a value is done in fp64; fp32 is used
+ * only where the inputs are fp32 (the logit comparisons that choose experts).
+ *
+ * Sources (page title, section):
+ *  - "Efficient and portable mixture-of-experts communication", Introduction:
+ *    a router produces a probability distribution over experts, the top-K
+ *    scoring experts are chosen and the layer output is the weighted average
+ *    of the chosen experts' outputs, weighted by values derived from that
+ *    distribution.  Sections "Dispatch" and "Combine": the sender counts the
+ *    tokens bound for every destination expert and packs token rows into
+ *    contiguous chunks; the receiver lays them out as contiguous per-expert
+ *    buffers for a grouped GEMM and keeps (rank, expert, token) so the
+ *    combine can find each row; the combine reads the K expert rows of a
+ *    token and forms their weighted sum into an externally allocated output.
+ *  - "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+ *    Training", Section 1: node-level deduplication -- a token crosses to a
+ *    node once however many of its experts live there; Section 3.1: the
+ *    task count sums to K*T.
+ *  - "Workload-Static Optical Circuit Switching for Scalable LLM Inference
+ *    Decode", section "Variable MoE Traffic and Regularization": the dispatch
+ *    traffic entry W_uv counts the rows sent from group u to group v;
+ *    production kernels size receive buffers for the worst case and drop
+ *    nothing.
+ *  - "MoX: Efficient MoE Routing on Direct-Connect Topologies", Section 2.1:
+ *    a per-token destination bitmap, 8 bytes at 64 endpoints.
+ *
+ * Readings where the pages leave a step open (ties to the lower expert index;
+ * selection by logit; softmax renormalised over the K chosen; experts placed
+ * on ranks, and ranks on nodes, in contiguous blocks; one packed row per
+ * (token, slot) in expert-major order with tokens ascending) are listed with
+ * the design notes of the repository.
+ *
+ * Parity pins: every function below is checked in the CPU test-suite against
+ * library routines (stable argsort, bincount, cumsum), closed forms and brute
+ * force; none of them is "parity unpinned".
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define REF_OK 0
+#define REF_EINVAL (-1)
+
+#define REF_DT_F32 0
+#define REF_DT_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* Scalar helpers                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Widen a bf16 bit pattern to its exact value. */
+static double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Round an fp64 value to the nearest bf16 (ties to even) in one step and
+ * return its bit pattern.  bf16 keeps 8 significant bits and the fp32
+ * exponent range; below 2^-126 the spacing is fixed at 2^-133. */
+uint16_t moe_ref_f64_to_bf16(double v) {
+  double a = fabs(v);
+  int neg = signbit(v) ? 1 : 0;
+  double q;
+  if (a == 0.0) {
+    q = 0.0;
+  } else {
+    int ex;
+    (void)frexp(a, &ex);          /* a = f * 2^ex, 0.5 <= f < 1 */
+    int shift = 8 - ex;           /* a * 2^shift lies in [128, 256) */
+    if (ex - 8 < -133) shift = 133; /* subnormal range: fixed quantum */
+    q = ldexp(nearbyint(ldexp(a, shift)), -shift);
+  }
+  float f = (float)(neg ? -q : q); /* exact: q is a bf16 value */
+  if (isinf(f) || fabs(q) >= ldexp(1.0, 128)) f = neg ? -INFINITY : INFINITY;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+/* "a ranks before b": larger logit first, equal logits by lower index.
+ * -0.0 and +0.0 compare equal under IEEE comparison, which is the wanted
+ * canonicalisation. */
+static int ranks_before(float la, int ia, float lb, int ib) {
+  if (la > lb) return 1;
+  if (la < lb) return 0;
+  return ia < ib;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 1. Gate                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* For every token t: choose the K experts that rank first under
+ * (logit descending, expert index ascending), in that order, by K passes of
+ * "take the best expert not yet taken".  Weights: softmax over the K chosen
+ * (renorm != 0) or the full softmax over E evaluated at the chosen experts
+ * (renorm == 0), in fp64 with the maximum subtracted, rounded once to fp32. */
+int moe_ref_gate(int T, int E, int K, int renorm, const float *logits,
+                 int32_t *topk_idx, float *topk_w) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return REF_EINVAL;
+  unsigned char taken[8192];
+  if (E > (int)sizeof taken) return REF_EINVAL;
+  for (int t = 0; t < T; ++t) {
+    const float *l = logits + (size_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int k = 0; k < K; ++k) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || ranks_before(l[e], e, l[best], best)) best = e;
+      }
+      taken[best] = 1;
+      topk_idx[(size_t)t * K + k] = best;
+    }
+    double m = (double)l[topk_idx[(size_t)t * K]]; /* the largest logit */
+    double denom = 0.0;
+    if (renorm) {
+      for (int k = 0; k < K; ++k)
+        denom += exp((double)l[topk_idx[(size_t)t * K + k]] - m);
+    } else {
+      for (int e = 0; e < E; ++e) denom += exp((double)l[e] - m);
+    }
+    for (int k = 0; k < K; ++k) {
+      double num = exp((double)l[topk_idx[(size_t)t * K + k]] - m);
+      topk_w[(size_t)t * K + k] = (float)(num / denom);
+    }
+  }
+  return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 2. Dispatch layout                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Experts sit on ranks in contiguous blocks of E/R, ranks on nodes in
+ * contiguous blocks of R/N.  Outputs (any of rank_token_count, node_mask,
+ * node_count, node_off, node_slot may be NULL):
+ *   expert_count[E]   rows bound for expert e
+ *   expert_off[E+1]   exclusive prefix sum of expert_count
+ *   rank_count[R]     rows bound for rank r (one row of the traffic matrix)
+ *   rank_off[R+1]     first row of rank r in the send buffer
+ *   rank_token_count[R] distinct tokens with at least one expert on rank r
+ *   node_mask[T]      bit n set when token t has an expert on node n
+ *   node_count[N]     tokens whose mask has bit n (one crossing per node)
+ *   node_off[N+1]     exclusive prefix sum of node_count
+ *   node_slot[T*N]    position of (t, n) in the node-major, token-ascending
+ *                     list of node crossings, or -1 when bit n is clear
+ *   slot_pos[T*K]     row of (t, k) in the send buffer: rows are grouped by
+ *                     expert in expert order; inside an expert, by (t, k)
+ *   row_src[T*K]      inverse permutation: row_src[slot_pos[i]] = i
+ * Returns REF_EINVAL for an expert id outside [0, E) or a bad shape. */
+int moe_ref_layout(int T, int E, int K, int R, int N,
+                   const int32_t *topk_idx, int32_t *expert_count,
+                   int32_t *expert_off, int32_t *rank_count, int32_t *rank_off,
+                   int32_t *rank_token_count, uint64_t *node_mask,
+                   int32_t *node_count, int32_t *node_off, int32_t *node_slot,
+                   int32_t *slot_pos, int32_t *row_src) {
+  if (T < 0 || E < 1 || K < 1 || R < 1 || N < 1 || N > 64) return REF_EINVAL;
+  if (E % R != 0 || R % N != 0) return REF_EINVAL;
+  const int per_rank = E / R;
+  const int per_node = R / N;
+  const size_t TK = (size_t)T * K;
+
+  for (size_t i = 0; i < TK; ++i)
+    if (topk_idx[i] < 0 || topk_idx[i] >= E) return REF_EINVAL;
+
+  /* (a) rows per expert and their exclusive scan */
+  for (int e = 0; e < E; ++e) expert_count[e] = 0;
+  for (size_t i = 0; i < TK; ++i) expert_count[topk_idx[i]] += 1;
+  expert_off[0] = 0;
+  for (int e = 0; e < E; ++e) expert_off[e + 1] = expert_off[e] + expert_count[e];
+
+  /* (b) rows per rank: experts of rank r are [r*E/R, (r+1)*E/R) */
+  for (int r = 0; r < R; ++r) {
+    int32_t c = 0;
+    for (int e = r * per_rank; e < (r + 1) * per_rank; ++e) c += expert_count[e];
+    rank_count[r] = c;
+  }
+  rank_off[0] = 0;
+  for (int r = 0; r < R; ++r) rank_off[r + 1] = rank_off[r] + rank_count[r];
+
+  /* (c) distinct tokens per rank */
+  if (rank_token_count) {
+    for (int r = 0; r < R; ++r) rank_token_count[r] = 0;
+    for (int t = 0; t < T; ++t) {
+      for (int r = 0; r < R; ++r) {
+        int hit = 0;
+        for (int k = 0; k < K; ++k)
+          if (topk_idx[(size_t)t * K + k] / per_rank == r) hit = 1;
+        rank_token_count[r] += hit;
+      }
+    }
+  }
+
+  /* (d) node dedup: one crossing per (token, distinct node) */
+  if (node_mask || node_count || node_off || node_slot) {
+    int32_t cnt[64];
+    int32_t seen[64];
+    for (int n = 0; n < N; ++n) cnt[n] = 0;
+    for (int t = 0; t < T; ++t) {
+      uint64_t m = 0;
+      for (int k = 0; k < K; ++k) {
+        int node = (topk_idx[(size_t)t * K + k] / per_rank) / per_node;
+        m |= (uint64_t)1 << node;
+      }
+      if (node_mask) node_mask[t] = m;
+      for (int n = 0; n < N; ++n)
+        if (m >> n & 1) cnt[n] += 1;
+    }
+    if (node_count)
+      for (int n = 0; n < N; ++n) node_count[n] = cnt[n];
+    int32_t off[65];
+    off[0] = 0;
+    for (int n = 0; n < N; ++n) off[n + 1] = off[n] + cnt[n];
+    if (node_off)
+      for (int n = 0; n <= N; ++n) node_off[n] = off[n];
+    if (node_slot) {
+      for (int n = 0; n < N; ++n) seen[n] = 0;
+      for (int t = 0; t < T; ++t) {
+        uint64_t m = 0;
+        for (int k = 0; k < K; ++k) {
+          int node = (topk_idx[(size_t)t * K + k] / per_rank) / per_node;
+          m |= (uint64_t)1 << node;
+        }
+        for (int n = 0; n < N; ++n) {
+          if (m >> n & 1) {
+            node_slot[(size_t)t * N + n] = off[n] + seen[n];
+            seen[n] += 1;
+          } else {
+            node_slot[(size_t)t * N + n] = -1;
+          }
+        }
+      }
+    }
+  }
+
+  /* (e) slot positions: walk (t, k) in order, each expert's rows fill its
+   * segment from the front */
+  for (int e = 0; e < E; ++e) expert_count[e] = 0; /* reuse as fill cursor */
+  for (size_t i = 0; i < TK; ++i) {
+    int e = topk_idx[i];
+    slot_pos[i] = expert_off[e] + expert_count[e];
+    expert_count[e] += 1;
+  }
+  /* expert_count is whole again: every cursor ended at its count */
+  for (size_t i = 0; i < TK; ++i) row_src[slot_pos[i]] = (int32_t)i;
+  return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 3. Pack                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* send[slot_pos[t*K+k]] = x[t], copied byte for byte (row_bytes per row). */
+int moe_ref_pack(int T, int K, size_t row_bytes, const void *x,
+                 const int32_t *slot_pos, void *send) {
+  if (T < 0 || K < 1) return REF_EINVAL;
+  const unsigned char *src = (const unsigned char *)x;
+  unsigned char *dst = (unsigned char *)send;
+  for (int t = 0; t < T; ++t) {
+    for (int k = 0; k < K; ++k) {
+      int32_t s = slot_pos[(size_t)t * K + k];
+      if (s < 0 || (size_t)s >= (size_t)T * K) return REF_EINVAL;
+      memcpy(dst + (size_t)s * row_bytes, src + (size_t)t * row_bytes,
+             row_bytes);
+    }
+  }
+  return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 4. Combine                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* out[t, h] = sum_k w[t,k] * s[e(t,k)] * y[slot_pos[t,k], h], summed in fp64
+ * in k order; s = 1 when expert_scale is NULL (expert ids then unused).
+ * out_exact (may be NULL) receives the unrounded fp64 sum; out (may be NULL)
+ * the sum rounded to nearest-even in out_dtype. */
+int moe_ref_combine(int T, int H, int K, int y_dtype, const void *y,
+                    const int32_t *slot_pos, const float *topk_w,
+                    const int32_t *topk_idx, const float *expert_scale,
+                    int out_dtype, void *out, double *out_exact) {
+  if (T < 0 || H < 1 || K < 1) return REF_EINVAL;
+  if (expert_scale && !topk_idx) return REF_EINVAL;
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) {
+        size_t i = (size_t)t * K + k;
+        double c = (double)topk_w[i];
+        if (expert_scale) c *= (double)expert_scale[topk_idx[i]];
+        size_t at = (size_t)slot_pos[i] * H + h;
+        double v = (y_dtype == REF_DT_F32) ? (double)((const float *)y)[at]
+                                           : bf16_value(((const uint16_t *)y)[at]);
+        acc += c * v;
+      }
+      size_t o = (size_t)t * H + h;
+      if (out_exact) out_exact[o] = acc;
+      if (out) {
+        if (out_dtype == REF_DT_F32)
+          ((float *)out)[o] = (float)acc;
+        else
+          ((uint16_t *)out)[o] = moe_ref_f64_to_bf16(acc);
+      }
+    }
+  }
+  return REF_OK;
+}
+
+/* Combine for a subset of tokens only (for sampled checks at full size):
+ * tokens[j] names the token whose row j of out/out_exact is produced. */
+int moe_ref_combine_tokens(int n_tokens, const int32_t *tokens, int H, int K,
+                           int y_dtype, const void *y,
+                           const int32_t *slot_pos, const float *topk_w,
+                           const int32_t *topk_idx, const float *expert_scale,
+                           double *out_exact) {
+  if (n_tokens < 0 || H < 1 || K < 1) return REF_EINVAL;
+  for (int j = 0; j < n_tokens; ++j) {
+    int t = tokens[j];
+    int r = moe_ref_combine(1, H, K, y_dtype,
+                            y, slot_pos + (size_t)t * K, topk_w + (size_t)t * K,
+                            topk_idx ? topk_idx + (size_t)t * K : NULL,
+                            expert_scale, REF_DT_F32, NULL,
+                            out_exact + (size_t)j * H);
+    if (r != REF_OK) return r;
+  }
+  return REF_OK;
+}
