@@ -1,0 +1,226 @@
+"""Benchmark of the MoE dispatch+combine hot path on one MI355X.
+
+One step = one call of moe_dispatch_combine (gate -> layout -> pack ->
+combine, the combine reading the packed rows back) over one batch of
+synthetic, seeded inputs already resident in HBM.  Prints one JSON line:
+tokens/s of the whole path, achieved HBM GB/s against the algorithmic bytes,
+a roofline entry for the dominant kernel (per-launch duration measured live
+with HIP events on the launch stream) and the CPU oracle timed on a bounded
+sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--workload deepseek_v3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs as mi  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1 MI355X"
+KERNEL_SOURCES = {
+    "pack": "combine_moe_topk_amd/csrc/pack.hip",
+    "combine": "combine_moe_topk_amd/csrc/combine.hip",
+}
+
+
+def kernel_bytes(w: mi.Workload) -> dict:
+    """Algorithmic bytes one launch of each row kernel must move."""
+    b, ob = w.elem_bytes, w.out_elem_bytes
+    T, H, K, E = w.T, w.H, w.K, w.E
+    return {
+        # x read once, K rows written, slot positions read
+        "pack": T * H * b + T * K * H * b + 4 * T * K,
+        # K rows read, one row written, slot/weight/expert id read, scales
+        "combine": T * K * H * b + T * H * ob + 12 * T * K + 4 * E,
+    }
+
+
+def source_digest(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries.
+
+    Null when no summary exists or the kernel source changed since the
+    counters were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        data = json.load(open(p))
+        ent = data[f"{kernel}/{workload}"]
+    except (KeyError, ValueError):
+        return None
+    if ent.get("source_sha") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w: mi.Workload, d: dict, sample_tokens: int) -> dict:
+    """The CPU oracle (single-threaded C) on the first tokens of the workload."""
+    import oracle
+
+    Ts = min(sample_tokens, w.T)
+    x = np.ascontiguousarray(d["x"][:Ts])
+    lg = np.ascontiguousarray(d["logits"][:Ts])
+    oracle.gate(lg[:2], w.K)  # load the library outside the timing
+    t0 = time.perf_counter()
+    oracle.dispatch_combine(x, lg, w.K, w.R, w.N, d["expert_scale"],
+                            w.out_dtype)
+    dt = time.perf_counter() - t0
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {Ts} of {w.T} tokens of {w.name}, whole path "
+                      f"(gate, layout, pack, combine), one thread, "
+                      f"{dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="deepseek_v3",
+                    choices=sorted(mi.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--fused-only", action="store_true",
+                    help="time only the fused call (for profiler runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this library does one GPU's "
+              "share of the dispatch/combine and uses no collectives; "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    w = mi.WORKLOADS[args.workload]
+    print(f"bench: workload {w.name} T={w.T} H={w.H} E={w.E} K={w.K} "
+          f"R={w.R} N={w.N}", file=sys.stderr, flush=True)
+    moe.lib()
+    d = mi.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    rows = torch.float32 if w.x_dtype == mi.F32 else torch.bfloat16
+    odt = torch.float32 if w.out_dtype == mi.F32 else torch.bfloat16
+    cfg = moe.make_cfg(w.T, w.H, w.E, w.K, w.R, w.N, w.x_dtype, w.out_dtype,
+                       w.renorm)
+    x, lg = to_dev(d["x"]), to_dev(d["logits"])
+    scale = None if d["expert_scale"] is None else to_dev(d["expert_scale"])
+    idx = torch.empty(w.T * w.K, dtype=torch.int32, device=dev)
+    wt = torch.empty(w.T * w.K, dtype=torch.float32, device=dev)
+    lay = moe.alloc_layout(cfg, dev)
+    send = torch.empty((w.T * w.K, w.H), dtype=rows, device=dev)
+    out = torch.empty((w.T, w.H), dtype=odt, device=dev)
+    ws = moe.alloc_workspace(cfg, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_dispatch_combine(cfg, x, lg, scale, idx, wt, lay, send, out,
+                                 ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if moe.moe_read_device_error(ws) != 0:
+        raise RuntimeError("device reported an input error")
+
+    # ---- timed region: exactly K fused steps --------------------------------
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"bench: fused {ms:.4f} ms/step (host clock {1e3 * t_host / args.steps:.4f})",
+          file=sys.stderr, flush=True)
+
+    tokens_per_s = w.T / (ms * 1e-3)
+    alg = w.algorithmic_bytes()
+    gbps = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.x_dtype == mi.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E,
+                   "K": w.K, "R": w.R, "N": w.N, "rows": w.x_dtype,
+                   "accumulate": "f32", "seed": w.seed},
+        "hbm": {"alg_bytes": alg, "gbps": gbps,
+                "frac_of_peak": gbps / HBM_PEAK_GBPS},
+    }
+
+    if not args.fused_only:
+        # ---- per-step launch durations (same stream, HIP events) ------------
+        def per_launch(fn, n):
+            starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            for i in range(n):
+                starts[i].record(stream)
+                fn()
+                ends[i].record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+        n = max(args.steps, 5)
+        steps_ms = {
+            "gate": per_launch(lambda: moe.moe_topk_gate(cfg, lg, idx, wt, stream), n),
+            "layout": per_launch(lambda: moe.moe_dispatch_layout(cfg, idx, lay, ws, stream), n),
+            "pack": per_launch(lambda: moe.moe_dispatch_pack(cfg, x, lay.slot_pos, send, stream), n),
+            "combine": per_launch(lambda: moe.moe_combine(cfg, send, lay.slot_pos, wt, idx, scale, out, stream), n),
+        }
+        result["steps_ms"] = steps_ms
+        kb = kernel_bytes(w)
+        dom = max(("pack", "combine"), key=lambda k: steps_ms[k])
+        achieved = kb[dom] / (steps_ms[dom] * 1e-3) / 1e9
+        traffic = load_traffic(dom, w.name)
+        result["roofline"] = {
+            "kernel": dom, "bound": "hbm", "achieved": achieved,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "alg_bytes_per_launch": kb[dom],
+            "launch_ms": steps_ms[dom],
+        }
+        for k in ("pack", "combine"):
+            result["roofline"][f"{k}_gbps"] = kb[k] / (steps_ms[k] * 1e-3) / 1e9
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

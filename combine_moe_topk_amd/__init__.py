@@ -1,0 +1,16 @@
+"""MI355X-native MoE token dispatch and combine (one GPU's share).
+
+The compute path is the HIP library ``libmoe_topk.so`` (C ABI in
+``include/moe_topk.h``); this package is its thin ctypes binding.  Names
+match the C entry points: :func:`moe_topk_gate`, :func:`moe_dispatch_layout`,
+:func:`moe_dispatch_pack`, :func:`moe_combine`, :func:`moe_dispatch_combine`.
+"""
+from ._lib import (  # noqa: F401
+    LAYOUT_FIELDS, Layout, MoeError, MOE_BF16, MOE_DEVERR_DUP_EXPERT,
+    MOE_DEVERR_EXPERT_RANGE, MOE_EINVAL, MOE_ELAUNCH, MOE_EUNSUPPORTED,
+    MOE_EWORKSPACE, MOE_F32, MOE_F_NO_RENORM, MOE_OK, alloc_layout,
+    alloc_workspace, lib, make_cfg, moe_cfg, moe_combine,
+    moe_dispatch_combine, moe_dispatch_layout, moe_dispatch_pack,
+    moe_layout, moe_read_device_error, moe_strerror, moe_topk_gate,
+    moe_validate_cfg, moe_version, moe_workspace_bytes, moe_workspace_init,
+)

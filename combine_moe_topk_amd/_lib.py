@@ -1,0 +1,278 @@
+"""ctypes binding of ``libmoe_topk.so`` (the C ABI in ``include/moe_topk.h``).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C calls.  PyTorch provides device memory and the HIP stream.  The
+library is loaded on first use; if it is missing the call raises instead of
+falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EWORKSPACE = -3
+MOE_ELAUNCH = -4
+
+MOE_DEVERR_EXPERT_RANGE = 0x1
+MOE_DEVERR_DUP_EXPERT = 0x2
+
+MOE_F32 = 0
+MOE_BF16 = 1
+MOE_F_NO_RENORM = 0x1
+
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16}
+TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {moe_strerror(code)} (code {code})")
+
+
+class moe_cfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("R", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("x_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("layout_tile", ctypes.c_int32)]
+
+
+class moe_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "expert_count", "expert_off", "rank_count", "rank_off",
+        "rank_token_count", "node_mask", "node_count", "node_off",
+        "node_slot", "slot_pos", "row_src")]
+
+
+LAYOUT_FIELDS = [n for n, _ in moe_layout._fields_]
+
+_LIB: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_CFG = ctypes.POINTER(moe_cfg)
+_LAY = ctypes.POINTER(moe_layout)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once); raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(
+                f"{_build.LIB} is missing: build it first with "
+                "`python -m combine_moe_topk_amd.build` (there is no "
+                "fallback implementation)")
+        L = ctypes.CDLL(_build.LIB)
+        sig = {
+            "moe_validate_cfg": (ctypes.c_int, [_CFG]),
+            "moe_workspace_bytes": (ctypes.c_size_t, [_CFG]),
+            "moe_workspace_init": (ctypes.c_int, [_P, ctypes.c_size_t, _P]),
+            "moe_topk_gate": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
+            "moe_dispatch_layout": (ctypes.c_int, [_CFG, _P, _LAY, _P,
+                                                   ctypes.c_size_t, _P]),
+            "moe_dispatch_pack": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
+            "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+            "moe_dispatch_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P,
+                                                    _LAY, _P, _P, _P,
+                                                    ctypes.c_size_t, _P]),
+            "moe_read_device_error": (ctypes.c_int, [_P, _P,
+                                                     ctypes.POINTER(ctypes.c_int32),
+                                                     ctypes.c_int]),
+            "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_version": (ctypes.c_int, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def make_cfg(T: int, H: int, E: int, K: int, R: int, N: int,
+             x_dtype: str = "bf16", out_dtype: str = "bf16",
+             renorm: bool = True, layout_tile: int = 0) -> moe_cfg:
+    return moe_cfg(T, H, E, K, R, N, DTYPE_CODE[x_dtype],
+                   DTYPE_CODE[out_dtype], 0 if renorm else MOE_F_NO_RENORM,
+                   layout_tile)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, what: str = "") -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, what)
+
+
+def moe_strerror(code: int) -> str:
+    return lib().moe_strerror(code).decode()
+
+
+def moe_version() -> int:
+    return lib().moe_version()
+
+
+def moe_validate_cfg(cfg: moe_cfg) -> int:
+    return lib().moe_validate_cfg(ctypes.byref(cfg))
+
+
+def moe_workspace_bytes(cfg: moe_cfg) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(cfg))
+
+
+def moe_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check(lib().moe_workspace_init(_ptr(ws, torch.uint8, "ws"), ws.numel(),
+                                    _stream(stream)), "moe_workspace_init")
+
+
+def moe_topk_gate(cfg: moe_cfg, logits: torch.Tensor, topk_idx: torch.Tensor,
+                  topk_w: torch.Tensor, stream=None) -> None:
+    _check(lib().moe_topk_gate(
+        ctypes.byref(cfg), _ptr(logits, torch.float32, "logits"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"), _stream(stream)),
+        "moe_topk_gate")
+
+
+@dataclasses.dataclass
+class Layout:
+    """Device tensors receiving the dispatch layout (see ``moe_layout``)."""
+
+    expert_count: torch.Tensor
+    expert_off: torch.Tensor
+    rank_count: torch.Tensor
+    rank_off: torch.Tensor
+    rank_token_count: Optional[torch.Tensor]
+    node_mask: Optional[torch.Tensor]
+    node_count: Optional[torch.Tensor]
+    node_off: Optional[torch.Tensor]
+    node_slot: Optional[torch.Tensor]
+    slot_pos: torch.Tensor
+    row_src: torch.Tensor
+
+    def c_struct(self) -> moe_layout:
+        vals = []
+        for name in LAYOUT_FIELDS:
+            t = getattr(self, name)
+            want = torch.int64 if name == "node_mask" else torch.int32
+            vals.append(_ptr(t, want, name))
+        return moe_layout(*vals)
+
+
+def alloc_layout(cfg: moe_cfg, device="cuda", optional: bool = True) -> Layout:
+    """Allocate layout outputs with torch (``node_mask`` as int64 bits)."""
+    def i32(n):
+        return torch.empty(max(n, 0), dtype=torch.int32, device=device)
+    T, E, K, R, N = cfg.T, cfg.E, cfg.K, cfg.R, cfg.N
+    return Layout(
+        expert_count=i32(E), expert_off=i32(E + 1), rank_count=i32(R),
+        rank_off=i32(R + 1),
+        rank_token_count=i32(R) if optional else None,
+        node_mask=(torch.empty(T, dtype=torch.int64, device=device)
+                   if optional else None),
+        node_count=i32(N) if optional else None,
+        node_off=i32(N + 1) if optional else None,
+        node_slot=i32(T * N) if optional else None,
+        slot_pos=i32(T * K), row_src=i32(T * K))
+
+
+def alloc_workspace(cfg: moe_cfg, device="cuda", init: bool = True,
+                    stream=None) -> torch.Tensor:
+    n = moe_workspace_bytes(cfg)
+    if n == 0:
+        raise MoeError(moe_validate_cfg(cfg), "moe_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("torch returned a workspace not aligned to 256 B")
+    if init:
+        moe_workspace_init(ws, stream)
+    return ws
+
+
+def moe_dispatch_layout(cfg: moe_cfg, topk_idx: torch.Tensor, layout: Layout,
+                        ws: torch.Tensor, stream=None) -> None:
+    lay = layout.c_struct()
+    _check(lib().moe_dispatch_layout(
+        ctypes.byref(cfg), _ptr(topk_idx, torch.int32, "topk_idx"),
+        ctypes.byref(lay), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_dispatch_layout")
+
+
+def _row_dtype(cfg: moe_cfg):
+    return TORCH_DTYPE[cfg.x_dtype]
+
+
+def moe_dispatch_pack(cfg: moe_cfg, x: torch.Tensor, slot_pos: torch.Tensor,
+                      send: torch.Tensor, stream=None) -> None:
+    _check(lib().moe_dispatch_pack(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(slot_pos, torch.int32, "slot_pos"),
+        _ptr(send, _row_dtype(cfg), "send"), _stream(stream)),
+        "moe_dispatch_pack")
+
+
+def moe_combine(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
+                topk_w: torch.Tensor, topk_idx: Optional[torch.Tensor],
+                expert_scale: Optional[torch.Tensor], out: torch.Tensor,
+                stream=None) -> None:
+    _check(lib().moe_combine(
+        ctypes.byref(cfg), _ptr(y, _row_dtype(cfg), "y"),
+        _ptr(slot_pos, torch.int32, "slot_pos"),
+        _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"), _stream(stream)),
+        "moe_combine")
+
+
+def moe_dispatch_combine(cfg: moe_cfg, x: torch.Tensor, logits: torch.Tensor,
+                         expert_scale: Optional[torch.Tensor],
+                         topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                         layout: Layout, send: torch.Tensor, out: torch.Tensor,
+                         ws: torch.Tensor, stream=None) -> None:
+    lay = layout.c_struct()
+    _check(lib().moe_dispatch_combine(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(lay),
+        _ptr(send, _row_dtype(cfg), "send"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+        "moe_dispatch_combine")
+
+
+def moe_read_device_error(ws: torch.Tensor, clear: bool = True,
+                          stream=None) -> int:
+    code = ctypes.c_int32(0)
+    _check(lib().moe_read_device_error(_ptr(ws, torch.uint8, "ws"),
+                                       _stream(stream), ctypes.byref(code),
+                                       int(bool(clear))),
+           "moe_read_device_error")
+    return code.value

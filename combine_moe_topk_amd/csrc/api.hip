@@ -1,0 +1,194 @@
+// Host side of the C ABI declared in include/moe_topk.h: argument validation,
+// workspace sizing, launch sequencing and error capture.  No call allocates,
+// synchronises (except moe_read_device_error) or keeps state between calls.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : 2; }
+
+int validate(const moe_cfg *c) {
+  if (!c) return MOE_EINVAL;
+  if (c->T < 0 || c->H < 1 || c->E < 1 || c->K < 1 || c->R < 1 || c->N < 1)
+    return MOE_EINVAL;
+  if (c->K > c->E || c->K > 32) return MOE_EINVAL;
+  if (c->E > 4096) return MOE_EINVAL;
+  if (c->E % c->R != 0 || c->R % c->N != 0 || c->N > 64) return MOE_EINVAL;
+  if ((int64_t)c->T * c->K > INT32_MAX) return MOE_EINVAL;
+  switch (c->layout_tile) {
+    case 0: case 64: case 128: case 256: case 512: case 1024: break;
+    default: return MOE_EINVAL;
+  }
+  if ((c->flags & ~MOE_F_NO_RENORM) != 0) return MOE_EINVAL;
+  if (c->x_dtype != MOE_F32 && c->x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
+    return MOE_EUNSUPPORTED;
+  if (c->H % 8 != 0) return MOE_EUNSUPPORTED;  // rows move in 8-element units
+  // one layout wave's LDS bitmaps must fit (see layout_geom)
+  if ((size_t)(c->E + c->R + c->N) * 8 > (size_t)moe::kLdsBudget ||
+      (size_t)(c->E + c->N) * 12 > (size_t)moe::kLdsBudget)
+    return MOE_EUNSUPPORTED;
+  if ((size_t)(c->E + c->R + c->N + c->E + 1) * 4 > (size_t)moe::kLdsBudget)
+    return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+int check_layout_ptrs(const moe_cfg *c, const moe_layout *l) {
+  if (!l) return MOE_EINVAL;
+  if (!l->expert_count || !l->expert_off || !l->rank_count || !l->rank_off)
+    return MOE_EINVAL;
+  if (c->T > 0 && (!l->slot_pos || !l->row_src)) return MOE_EINVAL;
+  if (l->node_mask && !aligned(l->node_mask, 8)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_ws(const moe_cfg *c, const void *ws, size_t ws_bytes) {
+  if (!ws) return MOE_EWORKSPACE;
+  if (!aligned(ws, 256)) return MOE_EUNSUPPORTED;
+  if (ws_bytes < moe::layout_geom(*c).ws_bytes) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint32_t v, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+namespace moe {
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t n,
+                           hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid), dim3(256), 0, stream, p,
+                     value, n);
+  return hipGetLastError();
+}
+}  // namespace moe
+
+extern "C" {
+
+int moe_validate_cfg(const moe_cfg *cfg) { return validate(cfg); }
+
+size_t moe_workspace_bytes(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  return moe::layout_geom(*cfg).ws_bytes;
+}
+
+int moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || ws_bytes < moe::kWsHeader) return MOE_EWORKSPACE;
+  if (!aligned(ws, 256)) return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_fill_u32(
+      (uint32_t *)ws, 0u, moe::kWsHeader / 4, stream));
+}
+
+int moe_topk_gate(const moe_cfg *cfg, const float *logits, int32_t *topk_idx,
+                  float *topk_w, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_EINVAL;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+    return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_gate(*cfg, logits, topk_idx, topk_w, stream));
+}
+
+int moe_dispatch_layout(const moe_cfg *cfg, const int32_t *topk_idx,
+                        const moe_layout *layout, void *ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->T > 0 && !topk_idx) return MOE_EINVAL;
+  if ((rc = check_layout_ptrs(cfg, layout)) != MOE_OK) return rc;
+  if ((rc = check_ws(cfg, ws, ws_bytes)) != MOE_OK) return rc;
+  return launch_status(moe::launch_layout(*cfg, topk_idx, *layout, ws, stream));
+}
+
+int moe_dispatch_pack(const moe_cfg *cfg, const void *x,
+                      const int32_t *slot_pos, void *send,
+                      hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !slot_pos || !send) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(send) || !aligned(slot_pos, 4))
+    return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_pack(*cfg, x, slot_pos, send, stream));
+}
+
+int moe_combine(const moe_cfg *cfg, const void *y, const int32_t *slot_pos,
+                const float *topk_w, const int32_t *topk_idx,
+                const float *expert_scale, void *out, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y || !slot_pos || !topk_w || !out) return MOE_EINVAL;
+  if (expert_scale && !topk_idx) return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(out)) return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_combine(*cfg, y, slot_pos, topk_w, topk_idx,
+                                           expert_scale, out, stream));
+}
+
+int moe_dispatch_combine(const moe_cfg *cfg, const void *x,
+                         const float *logits, const float *expert_scale,
+                         int32_t *topk_idx, float *topk_w,
+                         const moe_layout *layout, void *send, void *out,
+                         void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_layout_ptrs(cfg, layout)) != MOE_OK) return rc;
+  if ((rc = check_ws(cfg, ws, ws_bytes)) != MOE_OK) return rc;
+  if (cfg->T > 0) {
+    if (!x || !logits || !topk_idx || !topk_w || !send || !out)
+      return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(send) || !aligned16(out))
+      return MOE_EUNSUPPORTED;
+  }
+  hipError_t e = moe::launch_gate(*cfg, logits, topk_idx, topk_w, stream);
+  if (e == hipSuccess) e = moe::launch_layout(*cfg, topk_idx, *layout, ws, stream);
+  if (e == hipSuccess) e = moe::launch_pack(*cfg, x, layout->slot_pos, send, stream);
+  if (e == hipSuccess)
+    e = moe::launch_combine(*cfg, send, layout->slot_pos, topk_w, topk_idx,
+                            expert_scale, out, stream);
+  return launch_status(e);
+}
+
+int moe_read_device_error(const void *ws, hipStream_t stream,
+                          int32_t *host_code, int clear) {
+  if (!ws || !host_code) return MOE_EINVAL;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, ws, sizeof v, hipMemcpyDeviceToHost, stream) !=
+      hipSuccess)
+    return MOE_ELAUNCH;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ELAUNCH;
+  *host_code = v;
+  if (clear) {
+    if (moe::launch_fill_u32((uint32_t *)ws, 0u, 1, stream) != hipSuccess)
+      return MOE_ELAUNCH;
+  }
+  return MOE_OK;
+}
+
+const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "success";
+    case MOE_EINVAL: return "invalid argument or inconsistent shape";
+    case MOE_EUNSUPPORTED: return "unsupported dtype, alignment or size";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_ELAUNCH: return "HIP launch or copy failed";
+    default: return "unknown error code";
+  }
+}
+
+int moe_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+// Gate-weighted combine for gfx950:
+//   out[t,:] = sum_k w[t,k] * s[e(t,k)] * y[slot_pos[t,k], :]
+// accumulated in fp32 and rounded to nearest-even once into out's type.
+//
+// "Efficient and portable mixture-of-experts communication", section
+// "Combinación (Combine)": the receiver reads each token's K expert rows and
+// forms their weighted average into an externally allocated output; section
+// "Fragmentación e paralelismo": the accumulation is fused into the gather.
+//
+// HBM-bound gather: one wave per token.  Lane k < K loads (slot, weight*scale)
+// of slot k; the wave broadcasts them with readlane, so every row address is
+// scalar.  A pass covers UPL units of 8 elements per lane: all K*UPL 16-byte
+// row loads of a pass are independent and issued back to back (the pass size
+// is chosen from K so that about 16 loads are in flight per lane), then folded
+// into 8*UPL fp32 accumulators with FMAs, converted, and stored with
+// non-temporal 16-byte stores.  y rows are read exactly once.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// 8 elements of a row as fp32.
+template <bool BF16>
+struct Unit;
+
+template <>
+struct Unit<true> {  // 8 bf16 = one 16-byte vector
+  u32x4 v;
+  __device__ __forceinline__ void load(const char *row, int i) {
+    v = *(const u32x4 *)(row + (size_t)i * 16);
+  }
+  __device__ __forceinline__ float get(int j) const {
+    const uint32_t w = v[j >> 1];
+    return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+
+template <>
+struct Unit<false> {  // 8 fp32 = two 16-byte vectors
+  u32x4 a, b;
+  __device__ __forceinline__ void load(const char *row, int i) {
+    const u32x4 *p = (const u32x4 *)(row + (size_t)i * 32);
+    a = p[0];
+    b = p[1];
+  }
+  __device__ __forceinline__ float get(int j) const {
+    return __uint_as_float(j < 4 ? a[j] : b[j - 4]);
+  }
+};
+
+// fp32 -> bf16 bits, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <bool OBF16>
+__device__ __forceinline__ void store_unit(char *row, int i, const float *a) {
+  if constexpr (OBF16) {
+    u32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = bf16_rne(a[2 * j]) | (bf16_rne(a[2 * j + 1]) << 16);
+    __builtin_nontemporal_store(v, (u32x4 *)(row + (size_t)i * 16));
+  } else {
+    u32x4 v0, v1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v0[j] = __float_as_uint(a[j]);
+      v1[j] = __float_as_uint(a[4 + j]);
+    }
+    u32x4 *p = (u32x4 *)(row + (size_t)i * 32);
+    __builtin_nontemporal_store(v0, p);
+    __builtin_nontemporal_store(v1, p + 1);
+  }
+}
+
+// KT > 0: K known at compile time (fully unrolled); KT == 0: runtime K.
+template <bool YBF16, bool OBF16, int KT, int UPL>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const char *__restrict__ y, const int32_t *__restrict__ slot_pos,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ scale, char *__restrict__ out, int T, int Kr,
+    int U, int rows) {
+  const int K = KT > 0 ? KT : Kr;
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // one token per wave: uniform exit
+  const size_t ybytes = (size_t)U * (YBF16 ? 16 : 32);
+  const size_t obytes = (size_t)U * (OBF16 ? 16 : 32);
+
+  int my_slot = 0;
+  float my_c = 0.0f;
+  if (lane < K) {
+    const size_t i = (size_t)t * K + lane;
+    my_slot = slot_pos[i];
+    my_c = topk_w[i];
+    if (scale) my_c *= scale[topk_idx[i]];
+    if ((unsigned)my_slot >= (unsigned)rows) {  // out of range: adds 0
+      my_slot = 0;
+      my_c = 0.0f;
+    }
+  }
+  char *orow = out + (size_t)t * obytes;
+
+  for (int base = 0; base < U; base += kWave * UPL) {
+    float acc[UPL][8];
+#pragma unroll
+    for (int j = 0; j < UPL; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+
+    if constexpr (KT > 0) {
+      Unit<YBF16> u[KT][UPL];
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const int s = __builtin_amdgcn_readlane(my_slot, k);
+        const char *row = y + (size_t)s * ybytes;
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const int i = base + j * kWave + lane;
+          if (i < U) u[k][j].load(row, i);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const float c = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(my_c), k));
+#pragma unroll
+        for (int j = 0; j < UPL; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[j][e] = fmaf(c, u[k][j].get(e), acc[j][e]);
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const int s = __builtin_amdgcn_readlane(my_slot, k);
+        const float c = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(my_c), k));
+        const char *row = y + (size_t)s * ybytes;
+        Unit<YBF16> u[UPL];
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const int i = base + j * kWave + lane;
+          if (i < U) u[j].load(row, i);
+        }
+#pragma unroll
+        for (int j = 0; j < UPL; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[j][e] = fmaf(c, u[j].get(e), acc[j][e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+      const int i = base + j * kWave + lane;
+      if (i < U) store_unit<OBF16>(orow, i, acc[j]);
+    }
+  }
+}
+
+template <bool YB, bool OB, int KT>
+hipError_t launch_k(const moe_cfg &c, const void *y, const int32_t *slot_pos,
+                    const float *w, const int32_t *idx, const float *scale,
+                    void *out, hipStream_t s) {
+  // about 16 row loads (16 B each) in flight per lane per pass
+  constexpr int kLoadsPerUnit = YB ? 1 : 2;
+  constexpr int kK = KT > 0 ? KT : 4;
+  constexpr int kRaw = 16 / (kK * kLoadsPerUnit);
+  constexpr int UPL = kRaw < 1 ? 1 : (kRaw > 8 ? 8 : kRaw);
+  const int U = c.H / 8;
+  const int grid = (c.T + 3) / 4;
+  hipLaunchKernelGGL((combine_kernel<YB, OB, KT, UPL>), dim3(grid), dim3(256),
+                     0, s, (const char *)y, slot_pos, w, idx, scale,
+                     (char *)out, c.T, c.K, U, c.T * c.K);
+  return hipGetLastError();
+}
+
+template <bool YB, bool OB>
+hipError_t launch_d(const moe_cfg &c, const void *y, const int32_t *slot_pos,
+                    const float *w, const int32_t *idx, const float *scale,
+                    void *out, hipStream_t s) {
+  switch (c.K) {
+    case 1: return launch_k<YB, OB, 1>(c, y, slot_pos, w, idx, scale, out, s);
+    case 2: return launch_k<YB, OB, 2>(c, y, slot_pos, w, idx, scale, out, s);
+    case 4: return launch_k<YB, OB, 4>(c, y, slot_pos, w, idx, scale, out, s);
+    case 8: return launch_k<YB, OB, 8>(c, y, slot_pos, w, idx, scale, out, s);
+    case 16: return launch_k<YB, OB, 16>(c, y, slot_pos, w, idx, scale, out, s);
+    default: return launch_k<YB, OB, 0>(c, y, slot_pos, w, idx, scale, out, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_cfg &c, const void *y,
+                          const int32_t *slot_pos, const float *topk_w,
+                          const int32_t *topk_idx, const float *expert_scale,
+                          void *out, hipStream_t stream) {
+  if (c.T == 0) return hipSuccess;
+  const bool yb = c.x_dtype == MOE_BF16;
+  const bool ob = c.out_dtype == MOE_BF16;
+  if (yb && ob)
+    return launch_d<true, true>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
+  if (yb && !ob)
+    return launch_d<true, false>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
+  if (!yb && ob)
+    return launch_d<false, true>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
+  return launch_d<false, false>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,315 @@
+// Dispatch layout for gfx950: counts, exclusive offsets, node-level dedup and
+// the stable expert-major dispatch permutation, with no atomics whose order
+// could change a result.
+//
+// What is computed follows "Efficient and portable mixture-of-experts
+// communication", section "Envío (Dispatch)" (the sender counts the tokens
+// bound for every destination expert; the receiver packs them into contiguous
+// per-expert buffers and records where each row came from), "Workload-Static
+// Optical Circuit Switching for Scalable LLM Inference Decode", section
+// "Variable MoE Traffic and Regularization" (rows per destination group), and
+// "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+// Training", Section 1 (a token crosses to a node once, however many of its
+// experts live there).
+//
+// Design.  A workgroup owns a tile of 64*W consecutive tokens, one token per
+// lane.  For every wave and every expert (and rank, and node) it keeps a
+// 64-bit LDS bitmap of the wave's tokens that select it, built with LDS
+// atomicOr (order-free).  Then
+//   count of expert e in the tile          = sum over waves of popcount
+//   rank of (t, e) among earlier tile rows = popcount(bitmap & lanes-below)
+//                                            + popcounts of earlier waves
+// which is exactly the token-ascending order inside each expert, with no
+// sorting and no order-dependent atomics.  Three launches:
+//   count: per-tile column counts (experts | ranks | nodes) + node masks
+//   scan : one workgroup turns the count table into per-tile exclusive
+//          prefixes, totals, expert/rank/node offsets
+//   rank : rebuilds the tile bitmaps and writes slot_pos, row_src, node_slot
+// The count table lives in the caller's workspace: nblocks x (E + R + N).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void raise_error(int32_t *err, int bits) {
+  if (bits) atomicOr(err, bits);
+}
+
+__global__ __launch_bounds__(1024) void layout_count_kernel(
+    const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
+    int per_rank, int per_node_e, uint64_t *__restrict__ node_mask,
+    int32_t *__restrict__ table, int32_t *__restrict__ err) {
+  extern __shared__ uint64_t bm[];  // [W][cols]
+  const int cols = E + R + N;
+  const int W = blockDim.x / kWave;
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  for (int i = threadIdx.x; i < W * cols; i += blockDim.x) bm[i] = 0;
+  __syncthreads();
+
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t bit = 1ull << lane;
+  uint64_t *mine = bm + (size_t)w * cols;
+  int bad = 0;
+  if (t < T) {
+    uint64_t mask = 0;
+    const int32_t *row = idx + (size_t)t * K;
+    for (int k = 0; k < K; ++k) {
+      const int e = row[k];
+      if ((unsigned)e >= (unsigned)E) {
+        bad |= MOE_DEVERR_EXPERT_RANGE;
+        continue;
+      }
+      const uint64_t old = atomicOr((unsigned long long *)&mine[e], bit);
+      if (old & bit) bad |= MOE_DEVERR_DUP_EXPERT;
+      atomicOr((unsigned long long *)&mine[E + e / per_rank], bit);
+      mask |= 1ull << (e / per_node_e);
+    }
+    for (uint64_t m = mask; m; m &= m - 1)
+      atomicOr((unsigned long long *)&mine[E + R + __ffsll((long long)m) - 1],
+               bit);
+    if (node_mask) node_mask[t] = mask;
+  }
+  raise_error(err, bad);
+  __syncthreads();
+
+  int32_t *out = table + (size_t)blockIdx.x * cols;
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) {
+    int s = 0;
+    for (int v = 0; v < W; ++v) s += __popcll(bm[(size_t)v * cols + c]);
+    out[c] = s;
+  }
+}
+
+// Exclusive scan of n <= 4096 LDS values by one 1024-thread workgroup.
+// Writes out[0..n] (out[n] = total) to LDS.
+__device__ void block_exclusive_scan(const int32_t *in, int n, int32_t *out) {
+  __shared__ int32_t wsum[1024 / kWave];
+  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int lo = min(n, (int)threadIdx.x * per);
+  const int hi = min(n, lo + per);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) local += in[i];
+  // inclusive scan of `local` across the wave
+  const int lane = threadIdx.x % kWave;
+  int inc = local;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int v = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += v;
+  }
+  const int w = threadIdx.x / kWave;
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int v = 0; v < (int)(blockDim.x / kWave); ++v) {
+      const int s = wsum[v];
+      wsum[v] = run;
+      run += s;
+    }
+    out[n] = run;
+  }
+  __syncthreads();
+  int run = wsum[w] + inc - local;
+  for (int i = lo; i < hi; ++i) {
+    out[i] = run;
+    run += in[i];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void layout_scan_kernel(
+    int32_t *__restrict__ table, int nblocks, int E, int R, int N,
+    int per_rank, int32_t *__restrict__ expert_count,
+    int32_t *__restrict__ expert_off, int32_t *__restrict__ rank_count,
+    int32_t *__restrict__ rank_off, int32_t *__restrict__ rank_token_count,
+    int32_t *__restrict__ node_count, int32_t *__restrict__ node_off) {
+  extern __shared__ int32_t sm32[];
+  const int cols = E + R + N;
+  int32_t *tot = sm32;              // [cols]
+  int32_t *eoff = sm32 + cols;      // [E + 1]
+  // Column-wise exclusive prefix over the tiles, in place.
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) {
+    int run = 0;
+    int b = 0;
+    for (; b + 4 <= nblocks; b += 4) {
+      int32_t *p = table + (size_t)b * cols + c;
+      const int v0 = p[0], v1 = p[cols], v2 = p[2 * cols], v3 = p[3 * cols];
+      p[0] = run;
+      p[cols] = run + v0;
+      p[2 * cols] = run + v0 + v1;
+      p[3 * cols] = run + v0 + v1 + v2;
+      run += v0 + v1 + v2 + v3;
+    }
+    for (; b < nblocks; ++b) {
+      int32_t *p = table + (size_t)b * cols + c;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    tot[c] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan(tot, E, eoff);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    expert_count[e] = tot[e];
+    expert_off[e] = eoff[e];
+  }
+  if (threadIdx.x == 0) expert_off[E] = eoff[E];
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    rank_off[r] = eoff[r * per_rank];
+    rank_count[r] = eoff[(r + 1) * per_rank] - eoff[r * per_rank];
+    if (rank_token_count) rank_token_count[r] = tot[E + r];
+  }
+  if (threadIdx.x == 0) rank_off[R] = eoff[E];
+  // Tail row (index nblocks): global exclusive offsets of the expert and
+  // node columns, read by the rank kernel.
+  int32_t *tail = table + (size_t)nblocks * cols;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) tail[e] = eoff[e];
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int n = 0; n < N; ++n) {
+      const int v = tot[E + R + n];
+      if (node_count) node_count[n] = v;
+      if (node_off) node_off[n] = run;
+      tail[E + R + n] = run;
+      run += v;
+    }
+    if (node_off) node_off[N] = run;
+  }
+}
+
+__global__ __launch_bounds__(1024) void layout_rank_kernel(
+    const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
+    int per_node_e, const int32_t *__restrict__ table,
+    int32_t *__restrict__ slot_pos,
+    int32_t *__restrict__ row_src, int32_t *__restrict__ node_slot) {
+  extern __shared__ uint64_t sm[];
+  const int cr = E + N;  // expert bitmaps, then node bitmaps
+  const int cols = E + R + N;
+  const int W = blockDim.x / kWave;
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  uint64_t *bm = sm;                                  // [W][cr]
+  int32_t *base = (int32_t *)(sm + (size_t)W * cr);   // [cr]
+  for (int i = threadIdx.x; i < W * cr; i += blockDim.x) bm[i] = 0;
+  const int32_t *tile = table + (size_t)blockIdx.x * cols;
+  const int32_t *tail = table + (size_t)gridDim.x * cols;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) base[e] = tail[e] + tile[e];
+  if (node_slot)
+    for (int n = threadIdx.x; n < N; n += blockDim.x)
+      base[E + n] = tail[E + R + n] + tile[E + R + n];
+  __syncthreads();
+
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t bit = 1ull << lane;
+  const uint64_t below = bit - 1;
+  uint64_t *mine = bm + (size_t)w * cr;
+  uint64_t mask = 0;
+  if (t < T) {
+    const int32_t *row = idx + (size_t)t * K;
+    for (int k = 0; k < K; ++k) {
+      const int e = row[k];
+      if ((unsigned)e >= (unsigned)E) continue;
+      atomicOr((unsigned long long *)&mine[e], bit);
+      mask |= 1ull << (e / per_node_e);
+    }
+    if (node_slot)
+      for (uint64_t m = mask; m; m &= m - 1)
+        atomicOr((unsigned long long *)&mine[E + __ffsll((long long)m) - 1],
+                 bit);
+  }
+  __syncthreads();
+  if (t >= T) return;
+
+  const int32_t *row = idx + (size_t)t * K;
+  for (int k = 0; k < K; ++k) {
+    const size_t i = (size_t)t * K + k;
+    const int e = row[k];
+    if ((unsigned)e >= (unsigned)E) {
+      slot_pos[i] = -1;
+      continue;
+    }
+    int s = base[e] + __popcll(mine[e] & below);
+    for (int v = 0; v < w; ++v) s += __popcll(bm[(size_t)v * cr + e]);
+    slot_pos[i] = s;
+    row_src[s] = (int32_t)i;
+  }
+  if (node_slot) {
+    for (int n = 0; n < N; ++n) {
+      int s = -1;
+      if (mask >> n & 1) {
+        s = base[E + n] + __popcll(mine[E + n] & below);
+        for (int v = 0; v < w; ++v) s += __popcll(bm[(size_t)v * cr + E + n]);
+      }
+      node_slot[(size_t)t * N + n] = s;
+    }
+  }
+}
+
+}  // namespace
+
+LayoutGeom layout_geom(const moe_cfg &c) {
+  LayoutGeom g{};
+  g.cols = c.E + c.R + c.N;
+  const int want = c.layout_tile ? c.layout_tile : kDefaultLayoutTile;
+  int w = want / kWave;
+  // count kernel: W*cols*8 bytes; rank kernel: W*(E+N)*8 + (E+N)*4 bytes
+  while (w > 1 && ((size_t)w * g.cols * 8 > (size_t)kLdsBudget ||
+                   (size_t)w * (c.E + c.N) * 8 + (size_t)(c.E + c.N) * 4 >
+                       (size_t)kLdsBudget))
+    w >>= 1;
+  g.tile_waves = w;
+  g.tile_tokens = w * kWave;
+  g.nblocks = (c.T + g.tile_tokens - 1) / g.tile_tokens;
+  // one spare tail row after the per-tile rows carries global offsets
+  g.table_bytes = ((size_t)(g.nblocks + 1) * g.cols * 4 + 255) & ~(size_t)255;
+  g.ws_bytes = kWsHeader + g.table_bytes;
+  return g;
+}
+
+hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
+                         const moe_layout &lay, void *ws,
+                         hipStream_t stream) {
+  const LayoutGeom g = layout_geom(c);
+  int32_t *err = (int32_t *)ws;
+  int32_t *table = (int32_t *)((char *)ws + kWsHeader);
+  const int per_rank = c.E / c.R;
+  const int per_node_e = c.E / c.N;
+  const int threads = g.tile_tokens;
+
+  if (g.nblocks > 0) {
+    const size_t lds = (size_t)g.tile_waves * g.cols * 8;
+    hipLaunchKernelGGL(layout_count_kernel, dim3(g.nblocks), dim3(threads),
+                       lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
+                       per_rank, per_node_e, lay.node_mask, table, err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    // The scan leaves per-tile exclusive prefixes in rows [0, nblocks) and
+    // the global expert and node offsets in the tail row.
+    const size_t lds = (size_t)(g.cols + c.E + 1) * 4;
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(1024), lds, stream,
+                       table, g.nblocks, c.E, c.R, c.N, per_rank,
+                       lay.expert_count, lay.expert_off, lay.rank_count,
+                       lay.rank_off, lay.rank_token_count, lay.node_count,
+                       lay.node_off);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (g.nblocks > 0) {
+    const size_t lds = (size_t)g.tile_waves * (c.E + c.N) * 8 +
+                       (size_t)(c.E + c.N) * 4;
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.nblocks), dim3(threads),
+                       lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
+                       per_node_e, table, lay.slot_pos,
+                       lay.row_src, lay.node_slot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace moe

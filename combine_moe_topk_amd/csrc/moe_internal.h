@@ -1,0 +1,53 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of the MI355X MoE dispatch/combine library.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_topk.h"
+
+namespace moe {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr size_t kWsHeader = 256;    // workspace header: error word + pad
+constexpr int kLdsBudget = 65536;    // bytes of LDS a layout workgroup may use
+constexpr int kDefaultLayoutTile = 256;
+
+// 16-byte vector used for every row copy (one global_load/store_dwordx4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Launch geometry of the three layout kernels.  A layout workgroup owns a
+// tile of `tile_tokens` consecutive tokens, one token per lane, and keeps one
+// 64-bit token bitmap per (wave, expert / rank / node) in LDS.
+struct LayoutGeom {
+  int tile_waves;   // waves per workgroup
+  int tile_tokens;  // tile_waves * 64
+  int nblocks;      // ceil(T / tile_tokens)
+  int cols;         // E + R + N count columns per workgroup
+  size_t table_bytes;
+  size_t ws_bytes;  // header + nblocks * cols int32 (256-byte rounded)
+};
+
+LayoutGeom layout_geom(const moe_cfg &c);
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t n,
+                           hipStream_t stream);
+
+hipError_t launch_gate(const moe_cfg &c, const float *logits,
+                       int32_t *topk_idx, float *topk_w, hipStream_t stream);
+
+hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
+                         const moe_layout &lay, void *ws, hipStream_t stream);
+
+hipError_t launch_pack(const moe_cfg &c, const void *x,
+                       const int32_t *slot_pos, void *send,
+                       hipStream_t stream);
+
+hipError_t launch_combine(const moe_cfg &c, const void *y,
+                          const int32_t *slot_pos, const float *topk_w,
+                          const int32_t *topk_idx, const float *expert_scale,
+                          void *out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,75 @@
+// Dispatch pack for gfx950: send[slot_pos[t,k]] = x[t], bit for bit.
+//
+// "Efficient and portable mixture-of-experts communication", section
+// "Envío (Dispatch)": token rows are copied into contiguous chunks, one per
+// destination, before they are sent; on one GPU the destination chunks are
+// the expert-major segments of `send`.
+//
+// HBM-bound copy: each x row is read once into registers (16-byte vectors,
+// one wave per token, lanes striding the row so every load instruction moves
+// 1 KiB contiguously) and stored K times with non-temporal 16-byte stores,
+// since the packed rows are not re-read by this kernel and should not evict
+// anything from L2/MALL.  The K destination rows are scalar (wave-uniform):
+// lane k loads slot_pos[t,k] and the wave reads it back with readlane, so the
+// store addresses come from SGPRs.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <int VPL>
+__global__ __launch_bounds__(256) void pack_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ slot_pos,
+    u32x4 *__restrict__ send, int T, int K, int V, int rows) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // one token per wave: uniform exit
+  const int my_slot = lane < K ? slot_pos[(size_t)t * K + lane] : -1;
+  const u32x4 *src = x + (size_t)t * V;
+  for (int base = 0; base < V; base += kWave * VPL) {
+    u32x4 v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int i = base + j * kWave + lane;
+      if (i < V) v[j] = src[i];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int s = __builtin_amdgcn_readlane(my_slot, k);
+      if ((unsigned)s >= (unsigned)rows) continue;  // out-of-range: skipped
+      u32x4 *dst = send + (size_t)s * V;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int i = base + j * kWave + lane;
+        if (i < V) __builtin_nontemporal_store(v[j], dst + i);
+      }
+    }
+  }
+}
+
+template <int VPL>
+hipError_t launch_vpl(const void *x, const int32_t *slot_pos, void *send,
+                      int T, int K, int V, hipStream_t s) {
+  const int grid = (T + 3) / 4;
+  hipLaunchKernelGGL((pack_kernel<VPL>), dim3(grid), dim3(256), 0, s,
+                     (const u32x4 *)x, slot_pos, (u32x4 *)send, T, K, V,
+                     T * K);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack(const moe_cfg &c, const void *x,
+                       const int32_t *slot_pos, void *send,
+                       hipStream_t stream) {
+  if (c.T == 0) return hipSuccess;
+  const int b = c.x_dtype == MOE_F32 ? 4 : 2;
+  const int V = (int)((size_t)c.H * b / 16);  // 16-byte vectors per row
+  const int need = (V + kWave - 1) / kWave;
+  if (need <= 1) return launch_vpl<1>(x, slot_pos, send, c.T, c.K, V, stream);
+  if (need <= 2) return launch_vpl<2>(x, slot_pos, send, c.T, c.K, V, stream);
+  if (need <= 4) return launch_vpl<4>(x, slot_pos, send, c.T, c.K, V, stream);
+  if (need <= 8) return launch_vpl<8>(x, slot_pos, send, c.T, c.K, V, stream);
+  return launch_vpl<16>(x, slot_pos, send, c.T, c.K, V, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,214 @@
+/*
+ * moe_topk.h -- C ABI of the MI355X (gfx950) MoE dispatch/combine library.
+ *
+ * One GPU's share of Mixture-of-Experts token dispatch and combine, as four
+ * stream-ordered steps plus their composition:
+ *
+ *   moe_topk_gate        top-K experts per token and their gate weights
+ *   moe_dispatch_layout  counts, offsets, node-level dedup and the dispatch
+ *                        permutation
+ *   moe_dispatch_pack    hidden rows copied into contiguous per-rank,
+ *                        expert-major send buffers
+ *   moe_combine          expert rows gathered back to token order and summed
+ *                        with the gate weights
+ *   moe_dispatch_combine all four in order, the combine reading the packed
+ *                        rows back through a diagonal stand-in expert
+ *
+ * The problem statement these calls follow is the one in "Efficient and
+ * portable mixture-of-experts communication" (sections "Introdución",
+ * "Envío (Dispatch)" and "Combinación (Combine)"): dispatch consumes tokens plus routing and emits
+ * contiguous per-expert row buffers and per-token routing metadata; combine
+ * consumes expert rows, that metadata and the weights, and writes an
+ * externally allocated output; buffers are sized for the worst case; and no
+ * step needs a GPU-to-host round trip for counts.
+ *
+ * Notation: T tokens, H hidden size, E experts, K experts per token, R
+ * logical expert-parallel ranks holding E/R contiguous experts each, N
+ * logical nodes holding R/N contiguous ranks each.  Ranks and nodes are
+ * partitions of one GPU's buffers; nothing here talks to another GPU.
+ *
+ * Conventions for every call:
+ *  - All array arguments are DEVICE pointers to memory the caller owns
+ *    (allocated with hipMalloc or a framework allocator).  The library keeps
+ *    no pointer after a call returns, allocates nothing, and holds no
+ *    mutable global state.
+ *  - Every call validates its arguments on the host, enqueues its kernels on
+ *    `stream` and returns immediately.  Results are valid once the stream
+ *    reaches that point.  Nothing but moe_read_device_error synchronises.
+ *  - Row buffers (x, send, y, out) must be 16-byte aligned; other arrays
+ *    need their natural alignment.  Matrices are dense and row-major.
+ *  - Return value: MOE_OK, or a negative MOE_E* code; on error nothing is
+ *    enqueued (MOE_ELAUNCH: a launch failed after earlier ones of the same
+ *    call may have been enqueued).  Nothing throws across this ABI.
+ *  - Inputs never hold NaN; results for NaN logits or rows are unspecified.
+ */
+#ifndef MOE_TOPK_H
+#define MOE_TOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* null required pointer or inconsistent shape */
+#define MOE_EUNSUPPORTED (-2) /* valid but not supported: dtype, alignment   */
+#define MOE_EWORKSPACE (-3)   /* workspace missing or smaller than required  */
+#define MOE_ELAUNCH (-4)      /* a HIP launch or copy reported an error      */
+
+/* ---- device-detected input errors (bits of the workspace error word) --- */
+#define MOE_DEVERR_EXPERT_RANGE 0x1 /* a topk_idx entry outside [0, E)      */
+#define MOE_DEVERR_DUP_EXPERT 0x2   /* one token lists an expert twice      */
+
+/* ---- element types ----------------------------------------------------- */
+#define MOE_F32 0  /* IEEE binary32                                         */
+#define MOE_BF16 1 /* bfloat16 (upper half of binary32), ties-to-even       */
+
+/* ---- flags ------------------------------------------------------------- */
+/* Gate weights are the softmax over all E experts evaluated at the chosen
+ * ones, instead of the default softmax over the K chosen (which sums to 1). */
+#define MOE_F_NO_RENORM 0x1u
+
+/* Problem description shared by all calls. */
+typedef struct moe_cfg {
+  int32_t T;           /* tokens, >= 0                                        */
+  int32_t H;           /* hidden size, >= 1, multiple of 8                    */
+  int32_t E;           /* experts, 1..4096                                    */
+  int32_t K;           /* experts per token, 1..min(E, 32)                    */
+  int32_t R;           /* logical ranks, E % R == 0; rank(e) = e / (E/R)      */
+  int32_t N;           /* logical nodes, R % N == 0, N <= 64;
+                          node(r) = r / (R/N)                                 */
+  int32_t x_dtype;     /* MOE_F32 or MOE_BF16: x, send and y rows             */
+  int32_t out_dtype;   /* MOE_F32 or MOE_BF16: combine output                 */
+  uint32_t flags;      /* MOE_F_* bits                                        */
+  int32_t layout_tile; /* tokens per layout workgroup: 0 (default 256) or one
+                          of 64, 128, 256, 512, 1024.  Results do not depend
+                          on it; the workspace size does.                     */
+} moe_cfg;
+
+/* Outputs of the dispatch layout (device pointers, caller-allocated).
+ * Required: expert_count, expert_off, rank_count, rank_off, slot_pos,
+ * row_src.  Optional (NULL skips the output): rank_token_count, node_mask,
+ * node_count, node_off, node_slot. */
+typedef struct moe_layout {
+  int32_t *expert_count;     /* [E]   rows bound for expert e                  */
+  int32_t *expert_off;       /* [E+1] exclusive prefix sum of expert_count     */
+  int32_t *rank_count;       /* [R]   rows bound for rank r                    */
+  int32_t *rank_off;         /* [R+1] first send row of rank r                 */
+  int32_t *rank_token_count; /* [R]   distinct tokens with an expert on r      */
+  uint64_t *node_mask;       /* [T]   bit n: token has an expert on node n     */
+  int32_t *node_count;       /* [N]   tokens crossing to node n (once each)    */
+  int32_t *node_off;         /* [N+1] exclusive prefix sum of node_count       */
+  int32_t *node_slot;        /* [T*N] position of (t,n) in the node-major,
+                                token-ascending list of crossings, or -1      */
+  int32_t *slot_pos;         /* [T*K] send row of (t,k)                        */
+  int32_t *row_src;          /* [T*K] inverse: row_src[slot_pos[i]] == i       */
+} moe_layout;
+
+/* Host-only check of a configuration; touches no device.  Returns MOE_OK,
+ * MOE_EINVAL (bad shape) or MOE_EUNSUPPORTED (dtype, H alignment). */
+int moe_validate_cfg(const moe_cfg *cfg);
+
+/* Bytes of device workspace moe_dispatch_layout and moe_dispatch_combine
+ * need for `cfg` (a 256-byte header holding the device error word, then
+ * per-workgroup count tables).  0 when cfg is invalid.  Host only. */
+size_t moe_workspace_bytes(const moe_cfg *cfg);
+
+/* Clear the workspace header (the device error word).  Call once after
+ * allocating a workspace; the workspace can then be reused by any number of
+ * calls on the same stream.  Enqueued on `stream`. */
+int moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Top-K gate ("Efficient and portable mixture-of-experts communication",
+ * "Introdución": a router distribution over experts, the top-K scoring
+ * experts, a weighted average with weights from that distribution).
+ *   logits   [T*E] fp32 router scores, row-major by token.
+ *   topk_idx [T*K] int32 out: the K experts with the largest logits, in
+ *            descending logit order; equal logits go to the lower expert
+ *            index (-0.0 equals +0.0).
+ *   topk_w   [T*K] fp32 out: exp(l_k - l_max) / sum_j exp(l_j - l_max) over
+ *            the K chosen (MOE_F_NO_RENORM: over all E), computed in fp64
+ *            and rounded once to fp32. */
+int moe_topk_gate(const moe_cfg *cfg, const float *logits, int32_t *topk_idx,
+                  float *topk_w, hipStream_t stream);
+
+/* Dispatch layout (same page, "Envío (Dispatch)": per-destination token counts and
+ * contiguous per-expert buffers with (rank, expert, token) kept for the
+ * combine; "Workload-Static Optical Circuit Switching for Scalable LLM
+ * Inference Decode", "Variable MoE Traffic and Regularization": rows per
+ * destination group, worst-case buffers; "Cobalt: Leveraging Expert
+ * Co-activation for Efficient Distributed MoE Training", Section 1: a token
+ * crosses to a node once however many of its experts live there).
+ *   topk_idx [T*K] int32 expert ids; each row must list K distinct ids in
+ *            [0, E).  Violations set MOE_DEVERR_* bits in the workspace
+ *            error word; outputs are then unspecified but every write stays
+ *            in bounds (slot_pos entries of bad ids are -1).
+ *   layout   outputs, see moe_layout.  The send row order is expert-major
+ *            (expert 0's rows first) and, inside an expert, token-ascending;
+ *            rank r's rows are [rank_off[r], rank_off[r+1]).
+ *   ws       workspace of at least moe_workspace_bytes(cfg) bytes,
+ *            initialised once with moe_workspace_init. */
+int moe_dispatch_layout(const moe_cfg *cfg, const int32_t *topk_idx,
+                        const moe_layout *layout, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Dispatch pack ("Efficient and portable mixture-of-experts communication",
+ * "Envío (Dispatch)": token rows are packed into contiguous chunks per destination).
+ *   x        [T*H] rows of x_dtype.
+ *   slot_pos [T*K] send row of each (t,k), e.g. from moe_dispatch_layout.
+ *   send     [T*K*H] out, x_dtype: send[slot_pos[t*K+k]] = x[t], bit for
+ *            bit.  Rows no slot names are left untouched.  A slot outside
+ *            [0, T*K) is skipped. */
+int moe_dispatch_pack(const moe_cfg *cfg, const void *x,
+                      const int32_t *slot_pos, void *send,
+                      hipStream_t stream);
+
+/* Combine (same page, "Combinación (Combine)": the receiver reads the K expert rows of
+ * each token and forms their weighted average into an externally allocated
+ * output; "Fragmentación e paralelismo": the accumulation is fused into the
+ * gather).
+ *   y            [T*K*H] expert output rows of x_dtype, in send-row order.
+ *   slot_pos     [T*K] row of y holding (t,k); rows outside [0, T*K) add 0.
+ *   topk_w       [T*K] fp32 gate weights.
+ *   topk_idx     [T*K] int32 expert ids; read only when expert_scale is set.
+ *   expert_scale [E] fp32 or NULL: per-expert factor s_e applied to expert
+ *                e's rows (a diagonal stand-in expert); NULL means s = 1.
+ *   out          [T*H] out_dtype: sum_k w[t,k]*s[e(t,k)]*y[slot_pos[t,k]],
+ *                accumulated in fp32, rounded to nearest-even once. */
+int moe_combine(const moe_cfg *cfg, const void *y, const int32_t *slot_pos,
+                const float *topk_w, const int32_t *topk_idx,
+                const float *expert_scale, void *out, hipStream_t stream);
+
+/* The whole path on one GPU: gate -> layout -> pack -> combine, where the
+ * combine reads the packed rows back from `send` (on one GPU a rank's
+ * receive buffer is its own segment of send) through the diagonal stand-in
+ * expert s_e.  out is computed from send, never from x directly.  Outputs:
+ * topk_idx, topk_w, layout, send and out, each as in the calls above. */
+int moe_dispatch_combine(const moe_cfg *cfg, const void *x,
+                         const float *logits, const float *expert_scale,
+                         int32_t *topk_idx, float *topk_w,
+                         const moe_layout *layout, void *send, void *out,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Copy the workspace error word (MOE_DEVERR_* bits, 0 when clean) to
+ * *host_code after all work queued on `stream`; synchronises `stream`.  When
+ * `clear` is non-zero the word is reset to 0 afterwards (enqueued). */
+int moe_read_device_error(const void *ws, hipStream_t stream,
+                          int32_t *host_code, int clear);
+
+/* Static text for a MOE_* return code. */
+const char *moe_strerror(int code);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_TOPK_H */

@@ -13,7 +13,7 @@ patterns.
 
 Workload shapes follow the expert-parallel settings the pages discuss: the
 Mixtral/DeepSeek-V3 model families named in "Efficient and portable
-mixture-of-experts communication" (Introduction), DeepSeek-V3's 256 experts
+mixture-of-experts communication" ("Introdución"), DeepSeek-V3's 256 experts
 with top-8 and 7,168-wide BF16 embeddings in "MoX: Efficient MoE Routing on
 Direct-Connect Topologies" (Section 3, Methodology), and the skewed,
 co-activated expert demand described in MoX (Section 1) and in "Cobalt:

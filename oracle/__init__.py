@@ -5,11 +5,11 @@ benchmark's CPU-baseline leg, never by the library or its binding.  It shares
 no code with the HIP path; both are fed from ``moe_inputs``.
 
 Each function follows the definition stated in ``moe_ref.c`` (gate:
-"Efficient and portable mixture-of-experts communication", Introduction;
-layout: the same page's "Dispatch" section, Cobalt Section 1 for node-level
+"Efficient and portable mixture-of-experts communication", "Introdución";
+layout: the same page's "Envío (Dispatch)" section, Cobalt Section 1 for node-level
 deduplication and the OCS decode paper's "Variable MoE Traffic and
 Regularization" for per-destination row counts; pack and combine: the same
-blog's "Dispatch" and "Combine" sections).  All are pinned by the CPU tests.
+blog's "Envío (Dispatch)" and "Combinación (Combine)" sections).  All are pinned by the CPU tests.
 """
 from __future__ import annotations
 

@@ -10,11 +10,11 @@
  * only where the inputs are fp32 (the logit comparisons that choose experts).
  *
  * Sources (page title, section):
- *  - "Efficient and portable mixture-of-experts communication", Introduction:
+ *  - "Efficient and portable mixture-of-experts communication", "Introdución":
  *    a router produces a probability distribution over experts, the top-K
  *    scoring experts are chosen and the layer output is the weighted average
  *    of the chosen experts' outputs, weighted by values derived from that
- *    distribution.  Sections "Dispatch" and "Combine": the sender counts the
+ *    distribution.  Sections "Envío (Dispatch)" and "Combinación (Combine)": the sender counts the
  *    tokens bound for every destination expert and packs token rows into
  *    contiguous chunks; the receiver lays them out as contiguous per-expert
  *    buffers for a grouped GEMM and keeps (rank, expert, token) so the

@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and its host-only calls (validation, workspace sizing, error text)
+behave as documented.  No call here touches a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_moe_topk_amd as moe
+from combine_moe_topk_amd import build as libbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_topk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_topk_gate", "moe_dispatch_layout", "moe_dispatch_pack",
+              "moe_combine", "moe_dispatch_combine", "moe_workspace_bytes",
+              "moe_validate_cfg", "moe_read_device_error", "moe_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", libbuild.LIB],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_struct_layout_matches_header():
+    # the header's moe_cfg: ten 4-byte fields; moe_layout: eleven pointers
+    assert ctypes.sizeof(moe.moe_cfg) == 40
+    assert ctypes.sizeof(moe.moe_layout) == 11 * 8
+
+
+def cfg(**kw):
+    base = dict(T=16384, H=7168, E=256, K=8, R=64, N=8)
+    base.update(kw)
+    return moe.make_cfg(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, moe.MOE_OK),
+    ({"T": 0}, moe.MOE_OK),
+    ({"T": -1}, moe.MOE_EINVAL),
+    ({"H": 0}, moe.MOE_EINVAL),
+    ({"E": 0}, moe.MOE_EINVAL),
+    ({"K": 0}, moe.MOE_EINVAL),
+    ({"K": 257}, moe.MOE_EINVAL),
+    ({"K": 33, "E": 512, "R": 64}, moe.MOE_EINVAL),
+    ({"E": 250}, moe.MOE_EINVAL),          # E % R != 0
+    ({"R": 64, "N": 3}, moe.MOE_EINVAL),   # R % N != 0
+    ({"E": 8192, "R": 64}, moe.MOE_EINVAL),
+    ({"E": 128, "R": 128, "N": 128}, moe.MOE_EINVAL),  # N > 64
+    ({"T": 1 << 28, "K": 8}, moe.MOE_EINVAL),  # T*K overflows int32
+    ({"H": 7164}, moe.MOE_EUNSUPPORTED),   # not a multiple of 8
+    ({"x_dtype": "f32", "out_dtype": "bf16"}, moe.MOE_OK),
+    ({"layout_tile": 1024}, moe.MOE_OK),
+])
+def test_validate_cfg(kw, code):
+    assert moe.moe_validate_cfg(cfg(**kw)) == code
+
+
+def test_validate_rejects_bad_tile_flags_dtype():
+    c = cfg()
+    c.layout_tile = 100
+    assert moe.moe_validate_cfg(c) == moe.MOE_EINVAL
+    c = cfg()
+    c.flags = 0x80
+    assert moe.moe_validate_cfg(c) == moe.MOE_EINVAL
+    c = cfg()
+    c.x_dtype = 7
+    assert moe.moe_validate_cfg(c) == moe.MOE_EUNSUPPORTED
+    assert moe.lib().moe_validate_cfg(None) == moe.MOE_EINVAL
+
+
+def test_workspace_bytes():
+    c = cfg()
+    n = moe.moe_workspace_bytes(c)
+    # 256-byte header + (ceil(T/256) + 1) rows of (E + R + N) int32, rounded
+    rows = 16384 // 256 + 1
+    assert n == 256 + ((rows * (256 + 64 + 8) * 4 + 255) // 256) * 256
+    assert n % 256 == 0
+    assert moe.moe_workspace_bytes(cfg(T=-1)) == 0
+    # smaller tiles need more rows; results do not depend on the tile
+    assert moe.moe_workspace_bytes(cfg(layout_tile=64)) > n
+    # empty input still needs the header and the offsets row
+    assert moe.moe_workspace_bytes(cfg(T=0)) > 256
+
+
+def test_strerror_and_version():
+    assert moe.moe_strerror(0) == "success"
+    for c in (moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED, moe.MOE_EWORKSPACE,
+              moe.MOE_ELAUNCH):
+        assert moe.moe_strerror(c) != "unknown error code"
+    assert moe.moe_strerror(12345) == "unknown error code"
+    assert moe.moe_version() >= 10000
+
+
+def test_host_validation_before_any_device_work():
+    # invalid arguments are rejected on the host, so these calls return
+    # before touching HIP even on a machine without a GPU
+    lib = moe.lib()
+    c = cfg()
+    assert lib.moe_topk_gate(ctypes.byref(c), None, None, None, None) == moe.MOE_EINVAL
+    bad = cfg(E=250)
+    assert lib.moe_dispatch_pack(ctypes.byref(bad), None, None, None, None) == moe.MOE_EINVAL
+    lay = moe.moe_layout()
+    assert lib.moe_dispatch_layout(ctypes.byref(c), None, ctypes.byref(lay),
+                                   None, 0, None) == moe.MOE_EINVAL
+    assert lib.moe_workspace_init(None, 0, None) == moe.MOE_EWORKSPACE
+    assert lib.moe_read_device_error(None, None, None, 0) == moe.MOE_EINVAL

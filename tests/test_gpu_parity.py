@@ -1,0 +1,372 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer outputs (expert ids, counts, offsets, masks, slots, packed bytes) must
+be bit-exact; gate weights within 1e-6 relative; the combine within 1e-5
+relative (fp32 outputs) or 2e-2 absolute (bf16 outputs) of the oracle's
+unrounded fp64 sum.  Sizes: reduced-T shapes that span several layout tiles
+with a ragged tail, and every workload at its full size with the launch
+configuration the benchmark times (there, the combine is checked on sampled
+tokens and the packed buffer by a property over all rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_moe_topk_amd as moe
+import moe_inputs as mi
+import oracle
+from helpers import (ATOL_BF16, LAYOUT_KEYS, cfg_of, check_gate, check_layout,
+                     check_out, dev, host, layout_to_host, out_dtype,
+                     require_gpu, row_dtype, rows_f64, run_fused, term_scale)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    mi.TINY,
+    mi.DEEPSEEK_V3_DECODE,
+    mi.MIXTRAL.replace(T=1000, H=256),
+    mi.QWEN3.replace(T=777, H=512),
+    mi.DEEPSEEK_V3.replace(T=1000, H=520),
+    mi.KIMI.replace(T=600, H=256),
+]
+FULL = [mi.MIXTRAL, mi.QWEN3, mi.DEEPSEEK_V3, mi.KIMI]
+ALL = SMALL + FULL
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _ids(w):
+    return f"{w.name}-T{w.T}-H{w.H}"
+
+
+# ----------------------------------------------------------------- gate ----
+
+def gpu_gate(w, logits, renorm=True):
+    cfg = moe.make_cfg(w.T, w.H, w.E, w.K, w.R, w.N, w.x_dtype, w.out_dtype,
+                       renorm)
+    idx = torch.empty(w.T * w.K, dtype=torch.int32, device="cuda")
+    wt = torch.empty(w.T * w.K, dtype=torch.float32, device="cuda")
+    moe.moe_topk_gate(cfg, dev(logits), idx, wt)
+    return host(idx).reshape(w.T, w.K), host(wt).reshape(w.T, w.K)
+
+
+@pytest.mark.parametrize("w", ALL, ids=_ids)
+def test_gate(w):
+    lg = mi.make_inputs(w, with_x=False)["logits"]
+    ref_idx, ref_w = oracle.gate(lg, w.K)
+    idx, wt = gpu_gate(w, lg)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
+ADV = [("all_equal", lambda T, E, K: mi.logits_all_equal(T, E)),
+       ("signed_zeros", lambda T, E, K: mi.logits_signed_zeros(T, E, 5)),
+       ("few_levels", lambda T, E, K: mi.logits_few_levels(T, E, 3, 6)),
+       ("one_hot", lambda T, E, K: mi.logits_one_hot_experts(T, E, K, 3))]
+
+
+@pytest.mark.parametrize("name,make", ADV, ids=[a[0] for a in ADV])
+@pytest.mark.parametrize("E,K", [(8, 1), (8, 8), (16, 3), (64, 16),
+                                 (256, 8), (896, 16), (1000, 32), (4096, 5)])
+def test_gate_ties(name, make, E, K):
+    T = 300
+    w = mi.Workload("adv", T=T, H=8, E=E, K=K, R=1, N=1)
+    lg = make(T, E, K)
+    ref_idx, ref_w = oracle.gate(lg, K)
+    idx, wt = gpu_gate(w, lg)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
+def test_gate_no_renorm():
+    w = mi.DEEPSEEK_V3.replace(T=1000)
+    lg = mi.make_inputs(w, with_x=False)["logits"]
+    ref_idx, ref_w = oracle.gate(lg, w.K, renorm=False)
+    idx, wt = gpu_gate(w, lg, renorm=False)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
+# --------------------------------------------------------------- layout ----
+
+def gpu_layout(w, idx, layout_tile=0, optional=True):
+    cfg = cfg_of(w, layout_tile)
+    lay = moe.alloc_layout(cfg, optional=optional)
+    ws = moe.alloc_workspace(cfg)
+    moe.moe_dispatch_layout(cfg, dev(idx), lay, ws)
+    err = moe.moe_read_device_error(ws)
+    res = layout_to_host(lay, w.T, w.K, w.N)
+    res["dev_error"] = err
+    return res
+
+
+@pytest.mark.parametrize("tile", [0, 64, 1024])
+@pytest.mark.parametrize("w", ALL, ids=_ids)
+def test_layout(w, tile):
+    lg = mi.make_inputs(w, with_x=False)["logits"]
+    idx, _ = oracle.gate(lg, w.K)
+    ref = oracle.layout(idx, w.E, w.R, w.N)
+    res = gpu_layout(w, idx, tile)
+    assert res["dev_error"] == 0
+    check_layout(res, ref)
+
+
+@pytest.mark.parametrize("case", [
+    # T, E, K, R, N
+    (1, 8, 2, 4, 2), (63, 8, 8, 8, 8), (64, 16, 1, 16, 4), (65, 64, 16, 64, 64),
+    (257, 256, 8, 64, 8), (5000, 896, 16, 128, 16), (3000, 4, 4, 2, 1),
+    (2049, 128, 32, 128, 64)])
+def test_layout_random_ids(case):
+    T, E, K, R, N = case
+    idx = mi.random_topk_idx(T, E, K, seed=T)
+    w = mi.Workload("rand", T=T, H=8, E=E, K=K, R=R, N=N)
+    ref = oracle.layout(idx, E, R, N)
+    for tile in (0, 128):
+        res = gpu_layout(w, idx, tile)
+        assert res["dev_error"] == 0
+        check_layout(res, ref)
+
+
+def test_layout_one_hot_expert_set():
+    # every token picks the same K experts: K experts with T rows each
+    w = mi.DEEPSEEK_V3.replace(T=3000)
+    lg = mi.logits_one_hot_experts(w.T, w.E, w.K, first=250)
+    idx, _ = oracle.gate(lg, w.K)
+    ref = oracle.layout(idx, w.E, w.R, w.N)
+    check_layout(gpu_layout(w, idx), ref)
+
+
+def test_layout_without_optional_outputs():
+    w = mi.QWEN3.replace(T=999)
+    idx, _ = oracle.gate(mi.make_inputs(w, with_x=False)["logits"], w.K)
+    ref = oracle.layout(idx, w.E, w.R, w.N)
+    res = gpu_layout(w, idx, optional=False)
+    for k in ("rank_token_count", "node_mask", "node_count", "node_off",
+              "node_slot"):
+        assert k not in res
+    check_layout(res, ref)
+
+
+# ----------------------------------------------------------------- pack ----
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+def test_pack(w):
+    d = mi.make_inputs(w)
+    idx, _ = oracle.gate(d["logits"], w.K)
+    ref_lay = oracle.layout(idx, w.E, w.R, w.N)
+    ref_send = oracle.pack(d["x"], ref_lay["slot_pos"])
+    cfg = cfg_of(w)
+    send = torch.zeros((w.T * w.K, w.H), dtype=row_dtype(w), device="cuda")
+    moe.moe_dispatch_pack(cfg, dev(d["x"]), dev(ref_lay["slot_pos"]), send)
+    np.testing.assert_array_equal(host(send), ref_send)
+
+
+# -------------------------------------------------------------- combine ----
+
+@pytest.mark.parametrize("ydt,odt", [(mi.BF16, mi.BF16), (mi.F32, mi.F32),
+                                     (mi.BF16, mi.F32), (mi.F32, mi.BF16)])
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+def test_combine(w, ydt, odt):
+    w = w.replace(x_dtype=ydt, out_dtype=odt)
+    d = mi.make_inputs(w, with_x=False)
+    idx, wt = oracle.gate(d["logits"], w.K)
+    lay = oracle.layout(idx, w.E, w.R, w.N)
+    y = mi.random_x(w.T * w.K, w.H, ydt, seed=17)  # arbitrary expert outputs
+    scale = d["expert_scale"]
+    ref_out, exact = oracle.combine(y, lay["slot_pos"], wt, idx, scale, odt)
+    cfg = cfg_of(w)
+    out = torch.empty((w.T, w.H), dtype=out_dtype(w), device="cuda")
+    moe.moe_combine(cfg, dev(y), dev(lay["slot_pos"]), dev(wt), dev(idx),
+                    None if scale is None else dev(scale), out)
+    got = host(out)
+    coef = wt.astype(np.float64) * (1.0 if scale is None
+                                    else scale[idx].astype(np.float64))
+    check_out(got, exact, term_scale(rows_f64(y), lay["slot_pos"], coef), odt)
+    # almost every element also equals the oracle's own rounding
+    assert np.mean(got == ref_out) > 0.99
+
+
+# ---------------------------------------------------------------- fused ----
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids)
+def test_fused_small(w):
+    d = mi.make_inputs(w)
+    ref = oracle.dispatch_combine(d["x"], d["logits"], w.K, w.R, w.N,
+                                  d["expert_scale"], w.out_dtype)
+    res = run_fused(w, d)
+    assert res["dev_error"] == 0
+    check_gate(res, ref["topk_idx"], ref["topk_w"])
+    check_layout(res, ref)
+    np.testing.assert_array_equal(res["send"], ref["send"])
+    coef = ref["topk_w"].astype(np.float64)
+    if d["expert_scale"] is not None:
+        coef = coef * d["expert_scale"][ref["topk_idx"]]
+    check_out(res["out"], ref["out_exact"],
+              term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef),
+              w.out_dtype)
+
+
+@pytest.mark.parametrize("w", FULL, ids=_ids)
+def test_fused_full_size(w):
+    d = mi.make_inputs(w)
+    res = run_fused(w, d, keep_device=True)
+    assert res["dev_error"] == 0
+    idx, wt = oracle.gate(d["logits"], w.K)
+    check_gate(res, idx, wt)
+    lay = oracle.layout(idx, w.E, w.R, w.N)
+    check_layout(res, lay)
+    # every packed row is the x row the oracle's permutation names
+    src_tok = torch.from_numpy((lay["row_src"] // w.K).astype(np.int64)).cuda()
+    send, x = res["send_dev"], res["x_dev"]
+    for lo in range(0, w.T * w.K, 1 << 16):
+        hi = min(lo + (1 << 16), w.T * w.K)
+        assert torch.equal(send[lo:hi], x[src_tok[lo:hi]]), (lo, hi)
+    # sampled tokens: oracle's own pack and fp64 combine
+    ref_send = oracle.pack(d["x"], lay["slot_pos"])
+    rng = np.random.Generator(np.random.PCG64(5))
+    toks = np.unique(np.concatenate([[0, w.T - 1],
+                                     rng.integers(0, w.T, 254)])).astype(np.int32)
+    rows = lay["slot_pos"][toks].ravel()
+    np.testing.assert_array_equal(host(send[torch.from_numpy(rows).long().cuda()]),
+                                  ref_send[rows])
+    exact = oracle.combine_tokens(toks, ref_send, lay["slot_pos"], wt, idx,
+                                  d["expert_scale"])
+    coef = wt.astype(np.float64) * (1.0 if d["expert_scale"] is None
+                                    else d["expert_scale"][idx])
+    check_out(res["out"][toks], exact,
+              term_scale(rows_f64(ref_send), lay["slot_pos"], coef, toks),
+              w.out_dtype)
+
+
+# ----------------------------------------------------------- edge cases ----
+
+def test_empty_input():
+    w = mi.DEEPSEEK_V3.replace(T=0, H=64)
+    cfg = cfg_of(w)
+    lay = moe.alloc_layout(cfg)
+    lay.expert_count.fill_(-7)
+    lay.expert_off.fill_(-7)
+    ws = moe.alloc_workspace(cfg)
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    f = torch.empty(0, dtype=torch.float32, device="cuda")
+    xb = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    moe.moe_dispatch_combine(cfg, xb, f, None, e, f, lay, xb, xb, ws)
+    assert moe.moe_read_device_error(ws) == 0
+    assert torch.all(lay.expert_count == 0) and torch.all(lay.expert_off == 0)
+    assert torch.all(lay.node_off == 0) and torch.all(lay.rank_off == 0)
+
+
+@pytest.mark.parametrize("T,H,E,K,R,N,xdt,odt", [
+    (1, 8, 8, 2, 4, 2, mi.BF16, mi.BF16),      # one token, one unit per row
+    (1, 7168, 256, 8, 64, 8, mi.BF16, mi.BF16),
+    (130, 72, 16, 16, 4, 2, mi.BF16, mi.F32),  # K = E, 9 units: ragged lanes
+    (70, 1032, 8, 1, 8, 1, mi.F32, mi.F32),    # K = 1, 129 units
+    (200, 136, 32, 5, 8, 4, mi.F32, mi.BF16),  # K not a power of two
+    (129, 264, 64, 32, 64, 64, mi.BF16, mi.BF16),  # K = 32, N = 64
+])
+def test_fused_edge_shapes(T, H, E, K, R, N, xdt, odt):
+    w = mi.Workload("edge", T=T, H=H, E=E, K=K, R=R, N=N, x_dtype=xdt,
+                    out_dtype=odt, expert="mod8")
+    d = mi.make_inputs(w)
+    ref = oracle.dispatch_combine(d["x"], d["logits"], K, R, N,
+                                  d["expert_scale"], odt)
+    res = run_fused(w, d)
+    assert res["dev_error"] == 0
+    check_gate(res, ref["topk_idx"], ref["topk_w"])
+    check_layout(res, ref)
+    np.testing.assert_array_equal(res["send"], ref["send"])
+    coef = ref["topk_w"].astype(np.float64) * d["expert_scale"][ref["topk_idx"]]
+    check_out(res["out"], ref["out_exact"],
+              term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef), odt)
+
+
+def test_identity_experts_return_input():
+    # renormalised weights and identity experts: out == x (bf16), the dispatch
+    # permutation inverting exactly under the combine
+    w = mi.DEEPSEEK_V3.replace(T=2000, H=1024, expert="identity")
+    d = mi.make_inputs(w)
+    res = run_fused(w, d)
+    xf = mi.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    got = mi.bf16_bits_to_f32(res["out"]).astype(np.float64)
+    assert np.max(np.abs(got - xf)) <= ATOL_BF16
+    assert np.mean(res["out"] == d["x"]) > 0.999
+
+
+def test_one_hot_weights_invert_pack():
+    w = mi.KIMI.replace(T=500, H=512)
+    d = mi.make_inputs(w)
+    idx, _ = oracle.gate(d["logits"], w.K)
+    lay = oracle.layout(idx, w.E, w.R, w.N)
+    cfg = cfg_of(w)
+    send = torch.empty((w.T * w.K, w.H), dtype=torch.bfloat16, device="cuda")
+    sp = dev(lay["slot_pos"])
+    moe.moe_dispatch_pack(cfg, dev(d["x"]), sp, send)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    for k in (0, w.K - 1):
+        oh = np.zeros((w.T, w.K), np.float32)
+        oh[:, k] = 1.0
+        moe.moe_combine(cfg, send, sp, dev(oh), None, None, out)
+        np.testing.assert_array_equal(host(out), d["x"])
+
+
+# -------------------------------------------------------- determinism ----
+
+@pytest.mark.parametrize("w", [mi.QWEN3, mi.KIMI.replace(T=5000)], ids=_ids)
+def test_deterministic_across_runs_and_tiles(w):
+    d = mi.make_inputs(w)
+    a = run_fused(w, d, layout_tile=0)
+    b = run_fused(w, d, layout_tile=0)
+    c = run_fused(w, d, layout_tile=64)
+    e = run_fused(w, d, layout_tile=1024)
+    for other in (b, c, e):
+        for k in LAYOUT_KEYS + ("topk_idx", "topk_w", "send", "out"):
+            np.testing.assert_array_equal(a[k], other[k], err_msg=k)
+
+
+# ------------------------------------------------------ device errors ----
+
+def test_device_error_word():
+    w = mi.Workload("err", T=100, H=8, E=16, K=2, R=4, N=2)
+    idx = mi.random_topk_idx(w.T, w.E, w.K, seed=1)
+    assert gpu_layout(w, idx)["dev_error"] == 0
+    bad = idx.copy()
+    bad[7, 1] = 16
+    bad[9, 0] = -3
+    res = gpu_layout(w, bad)
+    assert res["dev_error"] == moe.MOE_DEVERR_EXPERT_RANGE
+    assert res["slot_pos"][7, 1] == -1 and res["slot_pos"][9, 0] == -1
+    ok = res["slot_pos"][res["slot_pos"] >= 0]
+    assert ok.max() < w.T * w.K
+    dup = idx.copy()
+    dup[3, 1] = dup[3, 0]
+    assert gpu_layout(w, dup)["dev_error"] == moe.MOE_DEVERR_DUP_EXPERT
+    # the word is sticky until read with clear
+    cfg = cfg_of(w)
+    lay = moe.alloc_layout(cfg)
+    ws = moe.alloc_workspace(cfg)
+    moe.moe_dispatch_layout(cfg, dev(bad), lay, ws)
+    moe.moe_dispatch_layout(cfg, dev(idx), lay, ws)
+    assert moe.moe_read_device_error(ws, clear=False) == 1
+    assert moe.moe_read_device_error(ws, clear=True) == 1
+    assert moe.moe_read_device_error(ws) == 0
+
+
+def test_host_errors_enqueue_nothing():
+    w = mi.DEEPSEEK_V3.replace(T=64, H=64)
+    cfg = cfg_of(w)
+    lay = moe.alloc_layout(cfg)
+    ws = moe.alloc_workspace(cfg)
+    small = ws[: moe.moe_workspace_bytes(cfg) - 256]
+    idx = torch.zeros(w.T * w.K, dtype=torch.int32, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_dispatch_layout(cfg, idx, lay, small)
+    assert ei.value.code == moe.MOE_EWORKSPACE
+    x = torch.zeros((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    send = torch.zeros((w.T * w.K * w.H + 1,), dtype=torch.bfloat16,
+                       device="cuda")
+    sp = torch.zeros(w.T * w.K, dtype=torch.int32, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_dispatch_pack(cfg, x, sp, send[1:])  # 2-byte aligned
+    assert ei.value.code == moe.MOE_EUNSUPPORTED
