@@ -184,8 +184,10 @@ def test_combine(w, ydt, odt):
     coef = wt.astype(np.float64) * (1.0 if scale is None
                                     else scale[idx].astype(np.float64))
     check_out(got, exact, term_scale(rows_f64(y), lay["slot_pos"], coef), odt)
-    # almost every element also equals the oracle's own rounding
-    assert np.mean(got == ref_out) > 0.99
+    if odt == mi.BF16:
+        # almost every bf16 element also equals the oracle's own rounding
+        # (fp32 outputs differ from the fp64 sum in the last bits by design)
+        assert np.mean(got == ref_out) > 0.99
 
 
 # ---------------------------------------------------------------- fused ----
