@@ -182,24 +182,29 @@ def main() -> int:
     }
 
     if not args.fused_only:
-        # ---- per-step launch durations (same stream, HIP events) ------------
-        def per_launch(fn, n):
-            starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-            ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-            for i in range(n):
-                starts[i].record(stream)
-                fn()
-                ends[i].record(stream)
-            torch.cuda.synchronize()
-            return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
-
+        # ---- per-kernel durations inside a real step ------------------------
+        # The four calls below launch exactly the kernels of one fused step,
+        # in the same order on the same stream; HIP events between them give
+        # each step's duration in the cache state a real step leaves behind.
         n = max(args.steps, 5)
-        steps_ms = {
-            "gate": per_launch(lambda: moe.moe_topk_gate(cfg, lg, idx, wt, stream), n),
-            "layout": per_launch(lambda: moe.moe_dispatch_layout(cfg, idx, lay, ws, stream), n),
-            "pack": per_launch(lambda: moe.moe_dispatch_pack(cfg, x, lay.slot_pos, send, stream), n),
-            "combine": per_launch(lambda: moe.moe_combine(cfg, send, lay.slot_pos, wt, idx, scale, out, stream), n),
-        }
+        names = ("gate", "layout", "pack", "combine")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+               for _ in range(n)]
+        for i in range(n):
+            e = evs[i]
+            e[0].record(stream)
+            moe.moe_topk_gate(cfg, lg, idx, wt, stream)
+            e[1].record(stream)
+            moe.moe_dispatch_layout(cfg, idx, lay, ws, stream)
+            e[2].record(stream)
+            moe.moe_dispatch_pack(cfg, x, lay.slot_pos, send, stream)
+            e[3].record(stream)
+            moe.moe_combine(cfg, send, lay.slot_pos, wt, idx, scale, out, stream)
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        steps_ms = {nm: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                       for i in range(n)]))
+                    for j, nm in enumerate(names)}
         result["steps_ms"] = steps_ms
         kb = kernel_bytes(w)
         dom = max(("pack", "combine"), key=lambda k: steps_ms[k])

@@ -7,13 +7,20 @@
 // forms their weighted average into an externally allocated output; section
 // "Fragmentación e paralelismo": the accumulation is fused into the gather.
 //
-// HBM-bound gather: one wave per token.  Lane k < K loads (slot, weight*scale)
-// of slot k; the wave broadcasts them with readlane, so every row address is
-// scalar.  A pass covers UPL units of 8 elements per lane: all K*UPL 16-byte
-// row loads of a pass are independent and issued back to back (the pass size
-// is chosen from K so that about 16 loads are in flight per lane), then folded
-// into 8*UPL fp32 accumulators with FMAs, converted, and stored with
-// non-temporal 16-byte stores.  y rows are read exactly once.
+// HBM-bound gather.  A token is owned by TPT threads (a whole workgroup of
+// 256 for wide rows, one wave of 64 for narrow ones); the threads stride the
+// row in units of 8 elements, so each load instruction of the group reads
+// TPT*16 contiguous bytes of one expert row.  Lane k < K of every wave loads
+// (slot, weight*scale) of slot k and the wave broadcasts them with readlane,
+// so row addresses are scalar.  A pass covers UPT units per thread: its K*UPT
+// 16-byte row loads are independent and issued back to back (UPT is chosen
+// from K so that about 16 loads are in flight per thread), then folded into
+// 8*UPT fp32 accumulators with FMAs, rounded and stored.  Row loads are
+// non-temporal (each y row is read exactly once) and so are the output
+// stores.  Measured on MI355X for the DeepSeek-V3 shape, with a pack before
+// every combine as in a real step: 404 us with 256 threads per token and
+// non-temporal loads, against 426 us for one wave per token and ordinary
+// loads.
 #include "moe_internal.h"
 
 namespace moe {
@@ -27,7 +34,7 @@ template <>
 struct Unit<true> {  // 8 bf16 = one 16-byte vector
   u32x4 v;
   __device__ __forceinline__ void load(const char *row, int i) {
-    v = *(const u32x4 *)(row + (size_t)i * 16);
+    v = __builtin_nontemporal_load((const u32x4 *)(row + (size_t)i * 16));
   }
   __device__ __forceinline__ float get(int j) const {
     const uint32_t w = v[j >> 1];
@@ -40,8 +47,8 @@ struct Unit<false> {  // 8 fp32 = two 16-byte vectors
   u32x4 a, b;
   __device__ __forceinline__ void load(const char *row, int i) {
     const u32x4 *p = (const u32x4 *)(row + (size_t)i * 32);
-    a = p[0];
-    b = p[1];
+    a = __builtin_nontemporal_load(p);
+    b = __builtin_nontemporal_load(p + 1);
   }
   __device__ __forceinline__ float get(int j) const {
     return __uint_as_float(j < 4 ? a[j] : b[j - 4]);
@@ -76,7 +83,8 @@ __device__ __forceinline__ void store_unit(char *row, int i, const float *a) {
 }
 
 // KT > 0: K known at compile time (fully unrolled); KT == 0: runtime K.
-template <bool YBF16, bool OBF16, int KT, int UPL>
+// TPT: threads per token (64 or 256); UPT: 8-element units per thread and pass.
+template <bool YBF16, bool OBF16, int KT, int UPT, int TPT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const char *__restrict__ y, const int32_t *__restrict__ slot_pos,
     const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
@@ -84,8 +92,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
     int U, int rows) {
   const int K = KT > 0 ? KT : Kr;
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;  // one token per wave: uniform exit
+  const int tt = threadIdx.x % TPT;  // thread within the token's group
+  const int t = blockIdx.x * (256 / TPT) + threadIdx.x / TPT;
+  if (t >= T) return;  // whole waves leave together (TPT is a wave multiple)
   const size_t ybytes = (size_t)U * (YBF16 ? 16 : 32);
   const size_t obytes = (size_t)U * (OBF16 ? 16 : 32);
 
@@ -103,22 +112,22 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
   char *orow = out + (size_t)t * obytes;
 
-  for (int base = 0; base < U; base += kWave * UPL) {
-    float acc[UPL][8];
+  for (int base = 0; base < U; base += TPT * UPT) {
+    float acc[UPT][8];
 #pragma unroll
-    for (int j = 0; j < UPL; ++j)
+    for (int j = 0; j < UPT; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
 
     if constexpr (KT > 0) {
-      Unit<YBF16> u[KT][UPL];
+      Unit<YBF16> u[KT][UPT];
 #pragma unroll
       for (int k = 0; k < KT; ++k) {
         const int s = __builtin_amdgcn_readlane(my_slot, k);
         const char *row = y + (size_t)s * ybytes;
 #pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const int i = base + j * kWave + lane;
+        for (int j = 0; j < UPT; ++j) {
+          const int i = base + j * TPT + tt;
           if (i < U) u[k][j].load(row, i);
         }
       }
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
         const float c = __int_as_float(
             __builtin_amdgcn_readlane(__float_as_int(my_c), k));
 #pragma unroll
-        for (int j = 0; j < UPL; ++j)
+        for (int j = 0; j < UPT; ++j)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             acc[j][e] = fmaf(c, u[k][j].get(e), acc[j][e]);
@@ -138,42 +147,54 @@ __global__ __launch_bounds__(256) void combine_kernel(
         const float c = __int_as_float(
             __builtin_amdgcn_readlane(__float_as_int(my_c), k));
         const char *row = y + (size_t)s * ybytes;
-        Unit<YBF16> u[UPL];
+        Unit<YBF16> u[UPT];
 #pragma unroll
-        for (int j = 0; j < UPL; ++j) {
-          const int i = base + j * kWave + lane;
+        for (int j = 0; j < UPT; ++j) {
+          const int i = base + j * TPT + tt;
           if (i < U) u[j].load(row, i);
         }
 #pragma unroll
-        for (int j = 0; j < UPL; ++j)
+        for (int j = 0; j < UPT; ++j)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             acc[j][e] = fmaf(c, u[j].get(e), acc[j][e]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      const int i = base + j * kWave + lane;
+    for (int j = 0; j < UPT; ++j) {
+      const int i = base + j * TPT + tt;
       if (i < U) store_unit<OBF16>(orow, i, acc[j]);
     }
   }
+}
+
+template <bool YB, bool OB, int KT, int TPT>
+hipError_t launch_kt(const moe_cfg &c, const void *y, const int32_t *slot_pos,
+                     const float *w, const int32_t *idx, const float *scale,
+                     void *out, hipStream_t s) {
+  // about 16 row loads (16 B each) in flight per thread per pass
+  constexpr int kLoadsPerUnit = YB ? 1 : 2;
+  constexpr int kK = KT > 0 ? KT : 4;
+  constexpr int kRaw = 16 / (kK * kLoadsPerUnit);
+  constexpr int UPT = kRaw < 1 ? 1 : (kRaw > 8 ? 8 : kRaw);
+  constexpr int kTokensPerBlock = 256 / TPT;
+  const int U = c.H / 8;
+  const int grid = (c.T + kTokensPerBlock - 1) / kTokensPerBlock;
+  hipLaunchKernelGGL((combine_kernel<YB, OB, KT, UPT, TPT>), dim3(grid),
+                     dim3(256), 0, s, (const char *)y, slot_pos, w, idx,
+                     scale, (char *)out, c.T, c.K, U, c.T * c.K);
+  return hipGetLastError();
 }
 
 template <bool YB, bool OB, int KT>
 hipError_t launch_k(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                     const float *w, const int32_t *idx, const float *scale,
                     void *out, hipStream_t s) {
-  // about 16 row loads (16 B each) in flight per lane per pass
-  constexpr int kLoadsPerUnit = YB ? 1 : 2;
-  constexpr int kK = KT > 0 ? KT : 4;
-  constexpr int kRaw = 16 / (kK * kLoadsPerUnit);
-  constexpr int UPL = kRaw < 1 ? 1 : (kRaw > 8 ? 8 : kRaw);
-  const int U = c.H / 8;
-  const int grid = (c.T + 3) / 4;
-  hipLaunchKernelGGL((combine_kernel<YB, OB, KT, UPL>), dim3(grid), dim3(256),
-                     0, s, (const char *)y, slot_pos, w, idx, scale,
-                     (char *)out, c.T, c.K, U, c.T * c.K);
-  return hipGetLastError();
+  // a whole workgroup per token once a row has at least 512 units
+  // (H >= 4096): each group-wide load then covers 4 KiB of a row
+  if (c.H / 8 >= 512)
+    return launch_kt<YB, OB, KT, 256>(c, y, slot_pos, w, idx, scale, out, s);
+  return launch_kt<YB, OB, KT, 64>(c, y, slot_pos, w, idx, scale, out, s);
 }
 
 template <bool YB, bool OB>

@@ -7,11 +7,13 @@
 //
 // HBM-bound copy: each x row is read once into registers (16-byte vectors,
 // one wave per token, lanes striding the row so every load instruction moves
-// 1 KiB contiguously) and stored K times with non-temporal 16-byte stores,
-// since the packed rows are not re-read by this kernel and should not evict
-// anything from L2/MALL.  The K destination rows are scalar (wave-uniform):
-// lane k loads slot_pos[t,k] and the wave reads it back with readlane, so the
-// store addresses come from SGPRs.
+// 1 KiB contiguously) and stored K times with ordinary 16-byte stores.  The K
+// destination rows are wave-uniform: lane k loads slot_pos[t,k] and the wave
+// reads it back with readlane, so the store addresses come from SGPRs.
+// Measured on MI355X with the combine running between packs (as in a real
+// step): ordinary stores, which the last-level cache can merge before they
+// reach HBM, beat non-temporal stores by ~11% (392 vs 441 us for the
+// DeepSeek-V3 shape), and reach the chip's plain copy rate (~5.4 TB/s).
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256) void pack_kernel(
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         const int i = base + j * kWave + lane;
-        if (i < V) __builtin_nontemporal_store(v[j], dst + i);
+        if (i < V) dst[i] = v[j];
       }
     }
   }
