@@ -100,6 +100,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--fused-only", action="store_true",
                     help="time only the fused call (for profiler runs)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run 3 plain device copies of this many MiB "
+                         "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -219,6 +222,17 @@ def main() -> int:
         }
         for k in ("pack", "combine"):
             result["roofline"][f"{k}_gbps"] = kb[k] / (steps_ms[k] * 1e-3) / 1e9
+
+    if args.copy_calib_mib > 0:
+        nb = args.copy_calib_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calib_bytes"] = nb
+        del src, dst
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)

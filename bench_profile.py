@@ -1,0 +1,138 @@
+"""Summarise rocprofv3 result databases of bench.py runs into profiles/.
+
+  python bench_profile.py trace  <results.db> <out.md> --cmd "<command>"
+  python bench_profile.py traffic <fetch.db> <write.db> --workload NAME \
+        --calib-mib MIB --cmd-fetch "<command>" --cmd-write "<command>"
+
+`trace` writes per-kernel duration statistics from a --kernel-trace run.
+`traffic` reads a FETCH_SIZE run and a WRITE_SIZE run of
+`bench.py --fused-only ... --copy-calib-mib MIB`, scales each counter by what
+it reads for the calibration copy (a device copy of MIB MiB, which reads and
+writes exactly MIB MiB), and records HBM bytes per launch of the pack and
+combine kernels in profiles/traffic.json together with the hash of each
+kernel's source (bench.py reports the figure only while the hash matches).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import json
+import os
+import re
+import sqlite3
+
+import bench
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def short(name: str) -> str:
+    m = re.search(r"(\w+_kernel(<[^>]*>)?)", name)
+    return m.group(1) if m else name[:48]
+
+
+def trace(db: str, out: str, cmd: str) -> None:
+    c = sqlite3.connect(db)
+    by = collections.defaultdict(list)
+    for n, d in c.execute("select name, duration from kernels"):
+        by[short(n)].append(d / 1000.0)
+    lines = [f"# Kernel trace summary\n", "Command:\n", f"    {cmd}\n",
+             "Per-dispatch durations (microseconds):\n", "```",
+             f"{'kernel':48s} {'n':>4s} {'avg':>10s} {'min':>10s} {'median':>10s} {'max':>10s}"]
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        lines.append(f"{k:48s} {len(v):4d} {sum(v) / len(v):10.3f} {v[0]:10.3f} "
+                     f"{v[len(v) // 2]:10.3f} {v[-1]:10.3f}")
+    lines.append("```\n")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+
+
+def _counter(db: str):
+    c = sqlite3.connect(db)
+    rows = list(c.execute(
+        "select dispatch_id, kernel_name, grid_size, value from "
+        "counters_collection order by dispatch_id"))
+    return rows
+
+
+def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
+            cmd_fetch: str, cmd_write: str) -> None:
+    fr, wr = _counter(fetch_db), _counter(write_db)
+    calib = calib_mib * 1024.0  # KiB read and written by the copy
+
+    def calib_kib(rows):
+        big = max((r for r in rows if "copyBuffer" in r[1]), key=lambda r: r[2])
+        vals = [r[3] for r in rows if "copyBuffer" in r[1] and r[2] == big[2]]
+        return sum(vals) / len(vals)
+
+    f_scale = calib / calib_kib(fr)
+    w_scale = calib / calib_kib(wr)
+
+    def per_kernel(rows):
+        by = collections.defaultdict(list)
+        for _, n, _, v in rows:
+            by[short(n)].append(v)
+        return {k: sum(v) / len(v) for k, v in by.items()}
+
+    fk, wk = per_kernel(fr), per_kernel(wr)
+    w = bench.mi.WORKLOADS[workload]
+    alg = bench.kernel_bytes(w)
+    path = os.path.join(PROFILES, "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    md = [f"# HBM traffic per launch: {workload}\n",
+          "Commands:\n", f"    {cmd_fetch}", f"    {cmd_write}\n",
+          f"Calibration: a device copy of {calib_mib} MiB reads "
+          f"{calib / f_scale / 1024:.1f} MiB as FETCH_SIZE and "
+          f"{calib / w_scale / 1024:.1f} MiB as WRITE_SIZE; counters are "
+          f"scaled by {f_scale:.3f} (fetch) and {w_scale:.3f} (write).\n",
+          "```",
+          f"{'kernel':42s} {'fetch MiB':>10s} {'write MiB':>10s} {'scaled MB':>10s} {'alg MB':>10s} {'ratio':>6s}"]
+    for k in sorted(fk, key=lambda k: -(fk[k] + wk.get(k, 0))):
+        fb = fk[k] * 1024 * f_scale
+        wb = wk.get(k, 0.0) * 1024 * w_scale
+        role = next((r for r in ("pack", "combine") if k.startswith(r)), None)
+        a = alg.get(role) if role else None
+        md.append(f"{k:42s} {fk[k] / 1024:10.1f} {wk.get(k, 0) / 1024:10.1f} "
+                  f"{(fb + wb) / 1e6:10.1f} "
+                  f"{(a / 1e6 if a else float('nan')):10.1f} "
+                  f"{((fb + wb) / a if a else float('nan')):6.3f}")
+        if role:
+            data[f"{role}/{workload}"] = {
+                "kernel": k, "bytes_per_launch": fb + wb, "fetch_bytes": fb,
+                "write_bytes": wb, "alg_bytes": a,
+                "fetch_scale": f_scale, "write_scale": w_scale,
+                "source_sha": bench.source_digest(bench.KERNEL_SOURCES[role]),
+            }
+    md.append("```\n")
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    with open(os.path.join(PROFILES, f"hbm_traffic_{workload}.md"), "w") as f:
+        f.write("\n".join(md))
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("out")
+    t.add_argument("--cmd", required=True)
+    r = sub.add_parser("traffic")
+    r.add_argument("fetch_db")
+    r.add_argument("write_db")
+    r.add_argument("--workload", default="deepseek_v3")
+    r.add_argument("--calib-mib", type=int, required=True)
+    r.add_argument("--cmd-fetch", required=True)
+    r.add_argument("--cmd-write", required=True)
+    a = ap.parse_args()
+    if a.what == "trace":
+        trace(a.db, a.out, a.cmd)
+    else:
+        traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
+                a.cmd_write)
+
+
+if __name__ == "__main__":
+    main()
