@@ -7,20 +7,21 @@
 // forms their weighted average into an externally allocated output; section
 // "Fragmentación e paralelismo": the accumulation is fused into the gather.
 //
-// HBM-bound gather.  A token is owned by TPT threads (a whole workgroup of
-// 256 for wide rows, one wave of 64 for narrow ones); the threads stride the
-// row in units of 8 elements, so each load instruction of the group reads
-// TPT*16 contiguous bytes of one expert row.  Lane k < K of every wave loads
-// (slot, weight*scale) of slot k and the wave broadcasts them with readlane,
-// so row addresses are scalar.  A pass covers UPT units per thread: its K*UPT
-// 16-byte row loads are independent and issued back to back (UPT is chosen
-// from K so that about 16 loads are in flight per thread), then folded into
-// 8*UPT fp32 accumulators with FMAs, rounded and stored.  Row loads are
-// non-temporal (each y row is read exactly once) and so are the output
-// stores.  Measured on MI355X for the DeepSeek-V3 shape, with a pack before
-// every combine as in a real step: 404 us with 256 threads per token and
-// non-temporal loads, against 426 us for one wave per token and ordinary
-// loads.
+// HBM-bound gather (K rows read per row written).  A token is owned by TPT
+// threads (64 or 256); the threads stride the row in units of 8 elements, so
+// each load instruction of the group reads TPT*16 contiguous bytes of one
+// expert row.  Lane k < K of every wave loads (slot, weight*scale) of slot k
+// and the wave broadcasts them with readlane, so row addresses are scalar.
+// Each thread owns UPT units of the row and issues all K*UPT of its 16-byte
+// row loads back to back before the first FMA: UPT is the largest value that
+// keeps about 32 loads (128 VGPRs of payload) in flight per thread, and TPT
+// the narrowest group for which TPT*UPT units cover the row, so a token takes
+// one pass when it fits.  Row loads are non-temporal (each y row is read
+// exactly once), and so are the output stores.  Measured on MI355X for the
+// DeepSeek-V3 shape (H=7168, K=8), with a pack before every combine as in a
+// real step: one pass of 32 loads per thread takes ~385 us against ~425 us
+// for two passes of 16, and non-temporal loads and stores beat ordinary ones
+// by ~20% and ~9%; the L2 scope bits (sc0/sc1) change nothing.
 #include "moe_internal.h"
 
 namespace moe {
@@ -84,6 +85,10 @@ __device__ __forceinline__ void store_unit(char *row, int i, const float *a) {
 
 // KT > 0: K known at compile time (fully unrolled); KT == 0: runtime K.
 // TPT: threads per token (64 or 256); UPT: 8-element units per thread and pass.
+// Row loads are branch-free: a unit index past the row end is clamped to the
+// row's last unit (an in-bounds address) and its value is never stored.  A
+// guarded load would sit in its own basic block, and the compiler then waits
+// for all outstanding loads before each one, serialising the K*UPT loads.
 template <bool YBF16, bool OBF16, int KT, int UPT, int TPT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const char *__restrict__ y, const int32_t *__restrict__ slot_pos,
@@ -126,10 +131,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
         const int s = __builtin_amdgcn_readlane(my_slot, k);
         const char *row = y + (size_t)s * ybytes;
 #pragma unroll
-        for (int j = 0; j < UPT; ++j) {
-          const int i = base + j * TPT + tt;
-          if (i < U) u[k][j].load(row, i);
-        }
+        for (int j = 0; j < UPT; ++j)
+          u[k][j].load(row, min(base + j * TPT + tt, U - 1));
       }
 #pragma unroll
       for (int k = 0; k < KT; ++k) {
@@ -149,10 +152,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
         const char *row = y + (size_t)s * ybytes;
         Unit<YBF16> u[UPT];
 #pragma unroll
-        for (int j = 0; j < UPT; ++j) {
-          const int i = base + j * TPT + tt;
-          if (i < U) u[j].load(row, i);
-        }
+        for (int j = 0; j < UPT; ++j)
+          u[j].load(row, min(base + j * TPT + tt, U - 1));
 #pragma unroll
         for (int j = 0; j < UPT; ++j)
 #pragma unroll
@@ -168,15 +169,20 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
+// Units per thread: about 32 16-byte row loads in flight per thread.
+template <bool YB, int KT>
+constexpr int upt_for() {
+  constexpr int kLoadsPerUnit = YB ? 1 : 2;
+  constexpr int kK = KT > 0 ? KT : 8;
+  constexpr int raw = 32 / (kK * kLoadsPerUnit);
+  return raw < 1 ? 1 : (raw > 8 ? 8 : raw);
+}
+
 template <bool YB, bool OB, int KT, int TPT>
 hipError_t launch_kt(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                      const float *w, const int32_t *idx, const float *scale,
                      void *out, hipStream_t s) {
-  // about 16 row loads (16 B each) in flight per thread per pass
-  constexpr int kLoadsPerUnit = YB ? 1 : 2;
-  constexpr int kK = KT > 0 ? KT : 4;
-  constexpr int kRaw = 16 / (kK * kLoadsPerUnit);
-  constexpr int UPT = kRaw < 1 ? 1 : (kRaw > 8 ? 8 : kRaw);
+  constexpr int UPT = upt_for<YB, KT>();
   constexpr int kTokensPerBlock = 256 / TPT;
   const int U = c.H / 8;
   const int grid = (c.T + kTokensPerBlock - 1) / kTokensPerBlock;
@@ -190,11 +196,10 @@ template <bool YB, bool OB, int KT>
 hipError_t launch_k(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                     const float *w, const int32_t *idx, const float *scale,
                     void *out, hipStream_t s) {
-  // a whole workgroup per token once a row has at least 512 units
-  // (H >= 4096): each group-wide load then covers 4 KiB of a row
-  if (c.H / 8 >= 512)
-    return launch_kt<YB, OB, KT, 256>(c, y, slot_pos, w, idx, scale, out, s);
-  return launch_kt<YB, OB, KT, 64>(c, y, slot_pos, w, idx, scale, out, s);
+  // one wave per token while 64*UPT units cover the row, else a workgroup
+  if (c.H / 8 <= 64 * upt_for<YB, KT>())
+    return launch_kt<YB, OB, KT, 64>(c, y, slot_pos, w, idx, scale, out, s);
+  return launch_kt<YB, OB, KT, 256>(c, y, slot_pos, w, idx, scale, out, s);
 }
 
 template <bool YB, bool OB>
