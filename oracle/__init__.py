@@ -9,7 +9,10 @@ Each function follows the definition stated in ``moe_ref.c`` (gate:
 layout: the same page's "Envío (Dispatch)" section, Cobalt Section 1 for node-level
 deduplication and the OCS decode paper's "Variable MoE Traffic and
 Regularization" for per-destination row counts; pack and combine: the same
-blog's "Envío (Dispatch)" and "Combinación (Combine)" sections).  All are pinned by the CPU tests.
+blog's "Envío (Dispatch)" and "Combinación (Combine)" sections; the two-leg
+node-level dispatch and the per-node partial combine: Cobalt Section 1 and
+"MoX: Efficient MoE Routing on Direct-Connect Topologies" Section 2.5).  All
+are pinned by the CPU tests.
 """
 from __future__ import annotations
 
@@ -46,8 +49,22 @@ def _lib() -> ctypes.CDLL:
             [_P] * 6)
         lib.moe_ref_f64_to_bf16.argtypes = [ctypes.c_double]
         lib.moe_ref_f64_to_bf16.restype = ctypes.c_uint16
+        lib.moe_ref_pack_nodes.argtypes = [ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_size_t, _P, _P,
+                                           ctypes.c_int, _P]
+        lib.moe_ref_forward.argtypes = ([ctypes.c_int] * 5 +
+                                        [ctypes.c_size_t, _P, ctypes.c_int] +
+                                        [_P] * 4)
+        lib.moe_ref_combine_partial.argtypes = (
+            [ctypes.c_int] * 7 + [_P] * 6 + [ctypes.c_int, ctypes.c_int,
+                                            _P, _P])
+        lib.moe_ref_combine_nodes.argtypes = (
+            [ctypes.c_int] * 4 + [_P, ctypes.c_int, _P, ctypes.c_int, _P,
+                                  _P])
         for f in ("moe_ref_gate", "moe_ref_layout", "moe_ref_pack",
-                  "moe_ref_combine", "moe_ref_combine_tokens"):
+                  "moe_ref_combine", "moe_ref_combine_tokens",
+                  "moe_ref_pack_nodes", "moe_ref_forward",
+                  "moe_ref_combine_partial", "moe_ref_combine_nodes"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -175,6 +192,115 @@ def combine_tokens(tokens: np.ndarray, y: np.ndarray, slot_pos: np.ndarray,
         _ptr(slot_pos), _ptr(topk_w), _ptr(topk_idx), _ptr(expert_scale),
         _ptr(exact)), "combine_tokens")
     return exact
+
+
+def node_rows(node_slot: np.ndarray) -> int:
+    """Rows of the leg-1 buffer: the number of (token, node) crossings."""
+    return int(np.count_nonzero(np.asarray(node_slot) >= 0))
+
+
+def pack_nodes(x: np.ndarray, node_slot: np.ndarray) -> np.ndarray:
+    """Leg 1: ``node_send[node_slot[t,n]] = x[t]`` for every crossing.
+
+    Returns node_send [D, H] with D = number of crossings.
+    """
+    x = np.ascontiguousarray(x)
+    node_slot = np.ascontiguousarray(node_slot, dtype=np.int32)
+    T, N = node_slot.shape
+    D = node_rows(node_slot)
+    out = np.zeros((D,) + x.shape[1:], dtype=x.dtype)
+    row_bytes = x[0].nbytes if T > 0 else 0
+    _check(_lib().moe_ref_pack_nodes(T, N, row_bytes, _ptr(x),
+                                     _ptr(node_slot), D, _ptr(out)),
+           "pack_nodes")
+    return out
+
+
+def forward(node_send: np.ndarray, node_slot: np.ndarray,
+            topk_idx: np.ndarray, slot_pos: np.ndarray, E: int,
+            R: int) -> np.ndarray:
+    """Leg 2: ``send[slot_pos[t,k]] = node_send[node_slot[t, node(e)]]``."""
+    node_send = np.ascontiguousarray(node_send)
+    node_slot = np.ascontiguousarray(node_slot, dtype=np.int32)
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    T, N = node_slot.shape
+    K = topk_idx.shape[1]
+    send = np.zeros((T * K,) + node_send.shape[1:], dtype=node_send.dtype)
+    row_bytes = node_send[0].nbytes if len(node_send) else 0
+    _check(_lib().moe_ref_forward(T, E, K, R, N, row_bytes, _ptr(node_send),
+                                  len(node_send), _ptr(node_slot),
+                                  _ptr(topk_idx), _ptr(slot_pos), _ptr(send)),
+           "forward")
+    return send
+
+
+def combine_partial(y: np.ndarray, slot_pos: np.ndarray, topk_w: np.ndarray,
+                    topk_idx: np.ndarray, expert_scale: Optional[np.ndarray],
+                    node_slot: np.ndarray, E: int, R: int,
+                    part_dtype: str = "bf16"):
+    """Per-node partial sums of each token's weighted expert rows.
+
+    Returns ``(part, exact)``: part [D, H] rounded to ``part_dtype`` and the
+    unrounded fp64 sums.
+    """
+    y = np.ascontiguousarray(y)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    node_slot = np.ascontiguousarray(node_slot, dtype=np.int32)
+    if expert_scale is not None:
+        expert_scale = np.ascontiguousarray(expert_scale, dtype=np.float32)
+    T, K = slot_pos.shape
+    N = node_slot.shape[1]
+    H = y.shape[1]
+    D = node_rows(node_slot)
+    pcode = DT_F32 if part_dtype == "f32" else DT_BF16
+    part = np.zeros((D, H), np.float32 if pcode == DT_F32 else np.uint16)
+    exact = np.zeros((D, H), np.float64)
+    _check(_lib().moe_ref_combine_partial(
+        T, H, E, K, R, N, _dtype_code(y), _ptr(y), _ptr(slot_pos),
+        _ptr(topk_w), _ptr(topk_idx), _ptr(expert_scale), _ptr(node_slot), D,
+        pcode, _ptr(part), _ptr(exact)), "combine_partial")
+    return part, exact
+
+
+def combine_nodes(part: np.ndarray, node_slot: np.ndarray,
+                  out_dtype: str = "bf16"):
+    """Sum of each token's node partials: ``(out, exact)`` as in combine."""
+    part = np.ascontiguousarray(part)
+    node_slot = np.ascontiguousarray(node_slot, dtype=np.int32)
+    T, N = node_slot.shape
+    H = part.shape[1]
+    ocode = DT_F32 if out_dtype == "f32" else DT_BF16
+    out = np.empty((T, H), np.float32 if ocode == DT_F32 else np.uint16)
+    exact = np.empty((T, H), np.float64)
+    _check(_lib().moe_ref_combine_nodes(
+        T, H, N, _dtype_code(part), _ptr(part), len(part), _ptr(node_slot),
+        ocode, _ptr(out), _ptr(exact)), "combine_nodes")
+    return out, exact
+
+
+def dispatch_combine_nodes(x: np.ndarray, logits: np.ndarray, K: int, R: int,
+                           N: int, expert_scale: Optional[np.ndarray] = None,
+                           out_dtype: str = "bf16", part_dtype: str = "bf16",
+                           renorm: bool = True) -> dict:
+    """The two-leg path: gate -> layout -> leg 1 -> leg 2 -> per-node
+    partials (Y = send) -> sum at the source."""
+    idx, w = gate(logits, K, renorm)
+    E = logits.shape[1]
+    lay = layout(idx, E, R, N)
+    node_send = pack_nodes(x, lay["node_slot"])
+    send = forward(node_send, lay["node_slot"], idx, lay["slot_pos"], E, R)
+    part, part_exact = combine_partial(send, lay["slot_pos"], w, idx,
+                                       expert_scale, lay["node_slot"], E, R,
+                                       part_dtype)
+    out, out_exact = combine_nodes(part, lay["node_slot"], out_dtype)
+    res = dict(lay)
+    res.update(topk_idx=idx, topk_w=w, node_send=node_send, send=send,
+               part=part, part_exact=part_exact, out=out,
+               out_exact=out_exact)
+    return res
 
 
 def f64_to_bf16(values) -> np.ndarray:

@@ -337,3 +337,144 @@ int moe_ref_combine_tokens(int n_tokens, const int32_t *tokens, int H, int K,
   }
   return REF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 5. Node-level two-leg dispatch and hierarchical combine                  */
+/* ------------------------------------------------------------------------ */
+/*
+ * "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+ * Training", Section 1: when several of a token's experts live on one remote
+ * node, the token crosses the inter-node link once and is forwarded inside
+ * the node.  "MoX: Efficient MoE Routing on Direct-Connect Topologies",
+ * Section 2.5: the combine runs the dispatch tree backwards and a node that
+ * holds several of a token's expert outputs reduces them before forwarding
+ * one vector toward the source.
+ *
+ * Leg 1 rows are node-major with tokens ascending inside a node: row
+ * node_slot[t*N+n] (from moe_ref_layout) carries token t to node n.  D is
+ * the number of such rows (the sum of node_count).
+ */
+
+/* Leg 1: node_send[node_slot[t*N+n]] = x[t] for every n with a slot >= 0. */
+int moe_ref_pack_nodes(int T, int N, size_t row_bytes, const void *x,
+                       const int32_t *node_slot, int D, void *node_send) {
+  if (T < 0 || N < 1 || D < 0) return REF_EINVAL;
+  const unsigned char *src = (const unsigned char *)x;
+  unsigned char *dst = (unsigned char *)node_send;
+  for (int t = 0; t < T; ++t) {
+    for (int n = 0; n < N; ++n) {
+      int32_t s = node_slot[(size_t)t * N + n];
+      if (s < 0) continue;
+      if (s >= D) return REF_EINVAL;
+      memcpy(dst + (size_t)s * row_bytes, src + (size_t)t * row_bytes,
+             row_bytes);
+    }
+  }
+  return REF_OK;
+}
+
+/* Leg 2: the row that reached expert e's node is copied to the expert's
+ * segment: send[slot_pos[t*K+k]] = node_send[node_slot[t*N + node(e)]] with
+ * e = topk_idx[t*K+k], node(e) = (e / (E/R)) / (R/N). */
+int moe_ref_forward(int T, int E, int K, int R, int N, size_t row_bytes,
+                    const void *node_send, int D, const int32_t *node_slot,
+                    const int32_t *topk_idx, const int32_t *slot_pos,
+                    void *send) {
+  if (T < 0 || E < 1 || K < 1 || R < 1 || N < 1) return REF_EINVAL;
+  if (E % R != 0 || R % N != 0) return REF_EINVAL;
+  const int per_rank = E / R, per_node = R / N;
+  const unsigned char *src = (const unsigned char *)node_send;
+  unsigned char *dst = (unsigned char *)send;
+  for (int t = 0; t < T; ++t) {
+    for (int k = 0; k < K; ++k) {
+      size_t i = (size_t)t * K + k;
+      int e = topk_idx[i];
+      if (e < 0 || e >= E) return REF_EINVAL;
+      int n = (e / per_rank) / per_node;
+      int32_t from = node_slot[(size_t)t * N + n];
+      int32_t to = slot_pos[i];
+      if (from < 0 || from >= D || to < 0 || (size_t)to >= (size_t)T * K)
+        return REF_EINVAL;
+      memcpy(dst + (size_t)to * row_bytes, src + (size_t)from * row_bytes,
+             row_bytes);
+    }
+  }
+  return REF_OK;
+}
+
+static double row_value(int dtype, const void *rows, size_t at) {
+  return dtype == REF_DT_F32 ? (double)((const float *)rows)[at]
+                             : bf16_value(((const uint16_t *)rows)[at]);
+}
+
+static void store_value(int dtype, void *rows, size_t at, double v) {
+  if (dtype == REF_DT_F32)
+    ((float *)rows)[at] = (float)v;
+  else
+    ((uint16_t *)rows)[at] = moe_ref_f64_to_bf16(v);
+}
+
+/* Reverse of leg 2, on the node: for every (t, n) with a slot,
+ *   part[node_slot[t*N+n], h] = sum over k with node(e(t,k)) = n of
+ *                                w[t,k] * s[e(t,k)] * y[slot_pos[t,k], h]
+ * summed in fp64 in k order (s = 1 when expert_scale is NULL).  part_exact
+ * (may be NULL) gets the unrounded sums, part (may be NULL) the sums rounded
+ * to nearest-even in part_dtype. */
+int moe_ref_combine_partial(int T, int H, int E, int K, int R, int N,
+                            int y_dtype, const void *y,
+                            const int32_t *slot_pos, const float *topk_w,
+                            const int32_t *topk_idx,
+                            const float *expert_scale,
+                            const int32_t *node_slot, int D, int part_dtype,
+                            void *part, double *part_exact) {
+  if (T < 0 || H < 1 || E < 1 || K < 1 || R < 1 || N < 1) return REF_EINVAL;
+  if (E % R != 0 || R % N != 0) return REF_EINVAL;
+  const int per_rank = E / R, per_node = R / N;
+  for (int t = 0; t < T; ++t) {
+    for (int n = 0; n < N; ++n) {
+      int32_t p = node_slot[(size_t)t * N + n];
+      if (p < 0) continue;
+      if (p >= D) return REF_EINVAL;
+      for (int h = 0; h < H; ++h) {
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) {
+          size_t i = (size_t)t * K + k;
+          int e = topk_idx[i];
+          if ((e / per_rank) / per_node != n) continue;
+          double c = (double)topk_w[i];
+          if (expert_scale) c *= (double)expert_scale[e];
+          acc += c * row_value(y_dtype, y, (size_t)slot_pos[i] * H + h);
+        }
+        size_t o = (size_t)p * H + h;
+        if (part_exact) part_exact[o] = acc;
+        if (part) store_value(part_dtype, part, o, acc);
+      }
+    }
+  }
+  return REF_OK;
+}
+
+/* Reverse of leg 1, at the source: out[t, h] = sum over n with a slot of
+ * part[node_slot[t*N+n], h], in fp64 in node order.  out_exact (may be NULL)
+ * gets the unrounded sums, out (may be NULL) the sums rounded to
+ * nearest-even in out_dtype. */
+int moe_ref_combine_nodes(int T, int H, int N, int part_dtype,
+                          const void *part, int D, const int32_t *node_slot,
+                          int out_dtype, void *out, double *out_exact) {
+  if (T < 0 || H < 1 || N < 1) return REF_EINVAL;
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int n = 0; n < N; ++n) {
+        int32_t p = node_slot[(size_t)t * N + n];
+        if (p < 0) continue;
+        if (p >= D) return REF_EINVAL;
+        acc += row_value(part_dtype, part, (size_t)p * H + h);
+      }
+      size_t o = (size_t)t * H + h;
+      if (out_exact) out_exact[o] = acc;
+      if (out) store_value(out_dtype, out, o, acc);
+    }
+  }
+  return REF_OK;
+}
