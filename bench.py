@@ -10,6 +10,12 @@ sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload deepseek_v3] [--no-cpu-baseline]
+                       [--path flat|two_leg] [--part-dtype bf16|f32]
+
+--path two_leg times moe_dispatch_combine_nodes instead: the node-level
+two-leg dispatch (one row per (token, node) crossing, then forwarded to the
+experts) and the hierarchical combine (per-node partial sums, then their sum
+at the source).
 """
 from __future__ import annotations
 
@@ -44,6 +50,22 @@ def kernel_bytes(w: mi.Workload) -> dict:
         "pack": T * H * b + T * K * H * b + 4 * T * K,
         # K rows read, one row written, slot/weight/expert id read, scales
         "combine": T * K * H * b + T * H * ob + 12 * T * K + 4 * E,
+    }
+
+
+def two_leg_kernel_bytes(w: mi.Workload, D: int, pb: int) -> dict:
+    """Algorithmic bytes per launch of the two-leg kernels; D = crossings."""
+    b, ob = w.elem_bytes, w.out_elem_bytes
+    T, H, K, N = w.T, w.H, w.K, w.N
+    return {
+        # x read once, one row per crossing written, node slots read
+        "pack_nodes": T * H * b + D * H * b + 4 * T * N,
+        # each crossing row read once, K rows written, routing read
+        "forward": D * H * b + T * K * H * b + T * (8 * K + 4 * N),
+        # K rows read, one partial row per crossing written, routing read
+        "partial": T * K * H * b + D * H * pb + T * (12 * K + 4 * N),
+        # partial rows read, one output row written, node slots read
+        "sum_nodes": D * H * pb + T * H * ob + 4 * T * N,
     }
 
 
@@ -100,6 +122,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--fused-only", action="store_true",
                     help="time only the fused call (for profiler runs)")
+    ap.add_argument("--path", default="flat", choices=("flat", "two_leg"))
+    ap.add_argument("--part-dtype", default="bf16", choices=("bf16", "f32"))
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -142,6 +166,9 @@ def main() -> int:
     out = torch.empty((w.T, w.H), dtype=odt, device=dev)
     ws = moe.alloc_workspace(cfg, dev)
     stream = torch.cuda.current_stream()
+    if args.path == "two_leg":
+        return two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out,
+                       ws, stream)
 
     def step():
         moe.moe_dispatch_combine(cfg, x, lg, scale, idx, wt, lay, send, out,
@@ -237,6 +264,103 @@ def main() -> int:
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)
 
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out, ws,
+            stream) -> int:
+    """Time moe_dispatch_combine_nodes (the two-leg path); one JSON line."""
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    dev = x.device
+    pdt = torch.bfloat16 if args.part_dtype == "bf16" else torch.float32
+    pb = 2 if args.part_dtype == "bf16" else 4
+    cap = moe.moe_node_rows_max(cfg)
+    ns = torch.empty((cap, w.H), dtype=x.dtype, device=dev)
+    part = torch.empty((cap, w.H), dtype=pdt, device=dev)
+
+    def step():
+        moe.moe_dispatch_combine_nodes(cfg, x, lg, scale, idx, wt, lay, ns,
+                                       send, part, out, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if moe.moe_read_device_error(ws) != 0:
+        raise RuntimeError("device reported an input error")
+    D = int(lay.node_off[-1].item())  # crossings (outside the timed region)
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"bench: two-leg {ms:.4f} ms/step, {D} crossings for "
+          f"{w.T * w.K} slots", file=sys.stderr, flush=True)
+
+    kb = two_leg_kernel_bytes(w, D, pb)
+    meta = w.T * (4 * w.E + 32 * w.K + 8 + 4 * w.N) + 8 * (w.E + w.R + w.N)
+    alg = sum(kb.values()) + meta
+    # per-kernel durations inside real steps (same launches, same order)
+    n = max(args.steps, 5)
+    names = ("gate", "layout", "pack_nodes", "forward", "partial", "sum_nodes")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)]
+           for _ in range(n)]
+    for i in range(n):
+        e = evs[i]
+        e[0].record(stream)
+        moe.moe_topk_gate(cfg, lg, idx, wt, stream)
+        e[1].record(stream)
+        moe.moe_dispatch_layout(cfg, idx, lay, ws, stream)
+        e[2].record(stream)
+        moe.moe_dispatch_pack_nodes(cfg, x, lay.node_slot, ns, stream)
+        e[3].record(stream)
+        moe.moe_dispatch_forward(cfg, ns, lay.node_slot, idx, lay.slot_pos,
+                                 send, stream)
+        e[4].record(stream)
+        moe.moe_combine_partial(cfg, send, lay.slot_pos, wt, idx, scale,
+                                lay.node_slot, part, stream)
+        e[5].record(stream)
+        moe.moe_combine_nodes(cfg, part, lay.node_slot, out, stream)
+        e[6].record(stream)
+    torch.cuda.synchronize()
+    steps_ms = {nm: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                   for i in range(n)]))
+                for j, nm in enumerate(names)}
+    dom = max(kb, key=lambda k: steps_ms[k])
+    achieved = kb[dom] / (steps_ms[dom] * 1e-3) / 1e9
+    gbps = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": w.T / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.x_dtype == mi.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "path": "two_leg", "T": w.T, "H": w.H,
+                   "E": w.E, "K": w.K, "R": w.R, "N": w.N, "rows": w.x_dtype,
+                   "partials": args.part_dtype, "accumulate": "f32",
+                   "seed": w.seed},
+        "hbm": {"alg_bytes": alg, "gbps": gbps,
+                "frac_of_peak": gbps / HBM_PEAK_GBPS},
+        "dedup": {"crossing_rows": D, "slot_rows": w.T * w.K,
+                  "inter_node_row_ratio": D / (w.T * w.K)},
+        "steps_ms": steps_ms,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "alg_bytes_per_launch": kb[dom],
+                     "launch_ms": steps_ms[dom],
+                     **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
+                        for k in kb}},
+    }
     print(json.dumps(result), flush=True)
     return 0
 

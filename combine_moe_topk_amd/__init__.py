@@ -3,7 +3,10 @@
 The compute path is the HIP library ``libmoe_topk.so`` (C ABI in
 ``include/moe_topk.h``); this package is its thin ctypes binding.  Names
 match the C entry points: :func:`moe_topk_gate`, :func:`moe_dispatch_layout`,
-:func:`moe_dispatch_pack`, :func:`moe_combine`, :func:`moe_dispatch_combine`.
+:func:`moe_dispatch_pack`, :func:`moe_combine`, :func:`moe_dispatch_combine`,
+and the node-level two-leg path :func:`moe_dispatch_pack_nodes`,
+:func:`moe_dispatch_forward`, :func:`moe_combine_partial`,
+:func:`moe_combine_nodes`, :func:`moe_dispatch_combine_nodes`.
 """
 from ._lib import (  # noqa: F401
     LAYOUT_FIELDS, Layout, MoeError, MOE_BF16, MOE_DEVERR_DUP_EXPERT,
@@ -13,4 +16,6 @@ from ._lib import (  # noqa: F401
     moe_dispatch_combine, moe_dispatch_layout, moe_dispatch_pack,
     moe_layout, moe_read_device_error, moe_strerror, moe_topk_gate,
     moe_validate_cfg, moe_version, moe_workspace_bytes, moe_workspace_init,
+    moe_node_rows_max, moe_dispatch_pack_nodes, moe_dispatch_forward,
+    moe_combine_partial, moe_combine_nodes, moe_dispatch_combine_nodes,
 )

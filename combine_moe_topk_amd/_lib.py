@@ -84,6 +84,18 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P,
                                                     _LAY, _P, _P, _P,
                                                     ctypes.c_size_t, _P]),
+            "moe_node_rows_max": (ctypes.c_size_t, [_CFG]),
+            "moe_dispatch_pack_nodes": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
+            "moe_dispatch_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P,
+                                                    _P]),
+            "moe_combine_partial": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P,
+                                                   _P, ctypes.c_int32, _P,
+                                                   _P]),
+            "moe_combine_nodes": (ctypes.c_int, [_CFG, _P, ctypes.c_int32, _P,
+                                                 _P, _P]),
+            "moe_dispatch_combine_nodes": (ctypes.c_int, [
+                _CFG, _P, _P, _P, _P, _P, _LAY, _P, _P, ctypes.c_int32, _P,
+                _P, _P, ctypes.c_size_t, _P]),
             "moe_read_device_error": (ctypes.c_int, [_P, _P,
                                                      ctypes.POINTER(ctypes.c_int32),
                                                      ctypes.c_int]),
@@ -266,6 +278,92 @@ def moe_dispatch_combine(cfg: moe_cfg, x: torch.Tensor, logits: torch.Tensor,
         _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
         "moe_dispatch_combine")
+
+
+# ---- node-level two-leg dispatch and hierarchical combine -----------------
+
+def moe_node_rows_max(cfg: moe_cfg) -> int:
+    """Rows of the leg-1 (node_send) and partial buffers: T * min(K, N)."""
+    return lib().moe_node_rows_max(ctypes.byref(cfg))
+
+
+def _part_code(part: torch.Tensor) -> int:
+    if part.dtype == torch.float32:
+        return MOE_F32
+    if part.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"part: expected float32 or bfloat16, got {part.dtype}")
+
+
+def moe_dispatch_pack_nodes(cfg: moe_cfg, x: torch.Tensor,
+                            node_slot: torch.Tensor, node_send: torch.Tensor,
+                            stream=None) -> None:
+    _check(lib().moe_dispatch_pack_nodes(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(node_slot, torch.int32, "node_slot"),
+        _ptr(node_send, _row_dtype(cfg), "node_send"), _stream(stream)),
+        "moe_dispatch_pack_nodes")
+
+
+def moe_dispatch_forward(cfg: moe_cfg, node_send: torch.Tensor,
+                         node_slot: torch.Tensor, topk_idx: torch.Tensor,
+                         slot_pos: torch.Tensor, send: torch.Tensor,
+                         stream=None) -> None:
+    _check(lib().moe_dispatch_forward(
+        ctypes.byref(cfg), _ptr(node_send, _row_dtype(cfg), "node_send"),
+        _ptr(node_slot, torch.int32, "node_slot"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(slot_pos, torch.int32, "slot_pos"),
+        _ptr(send, _row_dtype(cfg), "send"), _stream(stream)),
+        "moe_dispatch_forward")
+
+
+def moe_combine_partial(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
+                        topk_w: torch.Tensor, topk_idx: torch.Tensor,
+                        expert_scale: Optional[torch.Tensor],
+                        node_slot: torch.Tensor, part: torch.Tensor,
+                        stream=None) -> None:
+    _check(lib().moe_combine_partial(
+        ctypes.byref(cfg), _ptr(y, _row_dtype(cfg), "y"),
+        _ptr(slot_pos, torch.int32, "slot_pos"),
+        _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(node_slot, torch.int32, "node_slot"), _part_code(part),
+        _ptr(part, None, "part"), _stream(stream)), "moe_combine_partial")
+
+
+def moe_combine_nodes(cfg: moe_cfg, part: torch.Tensor,
+                      node_slot: torch.Tensor, out: torch.Tensor,
+                      stream=None) -> None:
+    _check(lib().moe_combine_nodes(
+        ctypes.byref(cfg), _ptr(part, None, "part"), _part_code(part),
+        _ptr(node_slot, torch.int32, "node_slot"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"), _stream(stream)),
+        "moe_combine_nodes")
+
+
+def moe_dispatch_combine_nodes(cfg: moe_cfg, x: torch.Tensor,
+                               logits: torch.Tensor,
+                               expert_scale: Optional[torch.Tensor],
+                               topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                               layout: Layout, node_send: torch.Tensor,
+                               send: torch.Tensor, part: torch.Tensor,
+                               out: torch.Tensor, ws: torch.Tensor,
+                               stream=None) -> None:
+    lay = layout.c_struct()
+    _check(lib().moe_dispatch_combine_nodes(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(lay),
+        _ptr(node_send, _row_dtype(cfg), "node_send"),
+        _ptr(send, _row_dtype(cfg), "send"), _part_code(part),
+        _ptr(part, None, "part"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+        "moe_dispatch_combine_nodes")
 
 
 def moe_read_device_error(ws: torch.Tensor, clear: bool = True,

@@ -162,6 +162,106 @@ int moe_dispatch_combine(const moe_cfg *cfg, const void *x,
   return launch_status(e);
 }
 
+size_t moe_node_rows_max(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  return (size_t)moe::node_rows_max(*cfg);
+}
+
+int moe_dispatch_pack_nodes(const moe_cfg *cfg, const void *x,
+                            const int32_t *node_slot, void *node_send,
+                            hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !node_slot || !node_send) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(node_send) || !aligned(node_slot, 4))
+    return MOE_EUNSUPPORTED;
+  return launch_status(
+      moe::launch_pack_nodes(*cfg, x, node_slot, node_send, stream));
+}
+
+int moe_dispatch_forward(const moe_cfg *cfg, const void *node_send,
+                         const int32_t *node_slot, const int32_t *topk_idx,
+                         const int32_t *slot_pos, void *send,
+                         hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->T == 0) return MOE_OK;
+  if (!node_send || !node_slot || !topk_idx || !slot_pos || !send)
+    return MOE_EINVAL;
+  if (!aligned16(node_send) || !aligned16(send)) return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_forward(*cfg, node_send, node_slot,
+                                           topk_idx, slot_pos, send, stream));
+}
+
+int moe_combine_partial(const moe_cfg *cfg, const void *y,
+                        const int32_t *slot_pos, const float *topk_w,
+                        const int32_t *topk_idx, const float *expert_scale,
+                        const int32_t *node_slot, int32_t part_dtype,
+                        void *part, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (part_dtype != MOE_F32 && part_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y || !slot_pos || !topk_w || !topk_idx || !node_slot || !part)
+    return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(part)) return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_partial(*cfg, y, slot_pos, topk_w,
+                                           topk_idx, expert_scale, node_slot,
+                                           part_dtype, part, stream));
+}
+
+int moe_combine_nodes(const moe_cfg *cfg, const void *part,
+                      int32_t part_dtype, const int32_t *node_slot, void *out,
+                      hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (part_dtype != MOE_F32 && part_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!part || !node_slot || !out) return MOE_EINVAL;
+  if (!aligned16(part) || !aligned16(out)) return MOE_EUNSUPPORTED;
+  return launch_status(
+      moe::launch_sum_nodes(*cfg, part, part_dtype, node_slot, out, stream));
+}
+
+int moe_dispatch_combine_nodes(const moe_cfg *cfg, const void *x,
+                               const float *logits, const float *expert_scale,
+                               int32_t *topk_idx, float *topk_w,
+                               const moe_layout *layout, void *node_send,
+                               void *send, int32_t part_dtype, void *part,
+                               void *out, void *ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (part_dtype != MOE_F32 && part_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if ((rc = check_layout_ptrs(cfg, layout)) != MOE_OK) return rc;
+  if ((rc = check_ws(cfg, ws, ws_bytes)) != MOE_OK) return rc;
+  if (cfg->T > 0) {
+    if (!x || !logits || !topk_idx || !topk_w || !node_send || !send ||
+        !part || !out || !layout->node_slot)
+      return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(node_send) || !aligned16(send) ||
+        !aligned16(part) || !aligned16(out))
+      return MOE_EUNSUPPORTED;
+  }
+  const moe_layout &l = *layout;
+  hipError_t e = moe::launch_gate(*cfg, logits, topk_idx, topk_w, stream);
+  if (e == hipSuccess) e = moe::launch_layout(*cfg, topk_idx, l, ws, stream);
+  if (e == hipSuccess)
+    e = moe::launch_pack_nodes(*cfg, x, l.node_slot, node_send, stream);
+  if (e == hipSuccess)
+    e = moe::launch_forward(*cfg, node_send, l.node_slot, topk_idx,
+                            l.slot_pos, send, stream);
+  if (e == hipSuccess)
+    e = moe::launch_partial(*cfg, send, l.slot_pos, topk_w, topk_idx,
+                            expert_scale, l.node_slot, part_dtype, part,
+                            stream);
+  if (e == hipSuccess)
+    e = moe::launch_sum_nodes(*cfg, part, part_dtype, l.node_slot, out,
+                              stream);
+  return launch_status(e);
+}
+
 int moe_read_device_error(const void *ws, hipStream_t stream,
                           int32_t *host_code, int clear) {
   if (!ws || !host_code) return MOE_EINVAL;

@@ -41,6 +41,12 @@ hipError_t launch_gate(const moe_cfg &c, const float *logits,
 hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
                          const moe_layout &lay, void *ws, hipStream_t stream);
 
+// send-style copy: dst[slots[t*W + w]] = x[t] for w < W (W <= 64), entries
+// outside [0, rows) skipped; row_bytes a multiple of 16.
+hipError_t launch_pack_rows(const void *x, const int32_t *slots, int W,
+                            int rows, void *dst, int T, int row_bytes,
+                            hipStream_t stream);
+
 hipError_t launch_pack(const moe_cfg &c, const void *x,
                        const int32_t *slot_pos, void *send,
                        hipStream_t stream);
@@ -49,5 +55,28 @@ hipError_t launch_combine(const moe_cfg &c, const void *y,
                           const int32_t *slot_pos, const float *topk_w,
                           const int32_t *topk_idx, const float *expert_scale,
                           void *out, hipStream_t stream);
+
+// Node-level two-leg dispatch and hierarchical combine (nodes.hip).  Leg-1
+// and partial buffers hold node_rows_max(c) = T * min(K, N) rows.
+int node_rows_max(const moe_cfg &c);
+
+hipError_t launch_pack_nodes(const moe_cfg &c, const void *x,
+                             const int32_t *node_slot, void *node_send,
+                             hipStream_t stream);
+
+hipError_t launch_forward(const moe_cfg &c, const void *node_send,
+                          const int32_t *node_slot, const int32_t *topk_idx,
+                          const int32_t *slot_pos, void *send,
+                          hipStream_t stream);
+
+hipError_t launch_partial(const moe_cfg &c, const void *y,
+                          const int32_t *slot_pos, const float *topk_w,
+                          const int32_t *topk_idx, const float *expert_scale,
+                          const int32_t *node_slot, int part_dtype,
+                          void *part, hipStream_t stream);
+
+hipError_t launch_sum_nodes(const moe_cfg &c, const void *part, int part_dtype,
+                            const int32_t *node_slot, void *out,
+                            hipStream_t stream);
 
 }  // namespace moe

@@ -9,7 +9,10 @@
 // one wave per token, lanes striding the row so every load instruction moves
 // 1 KiB contiguously) and stored K times with ordinary 16-byte stores.  The K
 // destination rows are wave-uniform: lane k loads slot_pos[t,k] and the wave
-// reads it back with readlane, so the store addresses come from SGPRs.
+// reads it back with readlane, so the store addresses come from SGPRs.  The
+// same kernel serves any table of W <= 64 destination rows per token (K for
+// the expert-major pack, N for the node-level pack); entries outside
+// [0, rows) are skipped.
 // Measured on MI355X with the combine running between packs (as in a real
 // step): ordinary stores, which the last-level cache can merge before they
 // reach HBM, beat non-temporal stores by ~11% (392 vs 441 us for the
@@ -22,11 +25,11 @@ namespace {
 template <int VPL>
 __global__ __launch_bounds__(256) void pack_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ slot_pos,
-    u32x4 *__restrict__ send, int T, int K, int V, int rows) {
+    u32x4 *__restrict__ send, int T, int W, int V, int rows) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // one token per wave: uniform exit
-  const int my_slot = lane < K ? slot_pos[(size_t)t * K + lane] : -1;
+  const int my_slot = lane < W ? slot_pos[(size_t)t * W + lane] : -1;
   const u32x4 *src = x + (size_t)t * V;
   for (int base = 0; base < V; base += kWave * VPL) {
     u32x4 v[VPL];
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(256) void pack_kernel(
       const int i = base + j * kWave + lane;
       if (i < V) v[j] = src[i];
     }
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < W; ++k) {
       const int s = __builtin_amdgcn_readlane(my_slot, k);
       if ((unsigned)s >= (unsigned)rows) continue;  // out-of-range: skipped
       u32x4 *dst = send + (size_t)s * V;
@@ -49,29 +52,35 @@ __global__ __launch_bounds__(256) void pack_kernel(
 }
 
 template <int VPL>
-hipError_t launch_vpl(const void *x, const int32_t *slot_pos, void *send,
-                      int T, int K, int V, hipStream_t s) {
+hipError_t launch_vpl(const void *x, const int32_t *slots, void *dst, int T,
+                      int W, int V, int rows, hipStream_t s) {
   const int grid = (T + 3) / 4;
   hipLaunchKernelGGL((pack_kernel<VPL>), dim3(grid), dim3(256), 0, s,
-                     (const u32x4 *)x, slot_pos, (u32x4 *)send, T, K, V,
-                     T * K);
+                     (const u32x4 *)x, slots, (u32x4 *)dst, T, W, V, rows);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_pack_rows(const void *x, const int32_t *slots, int W,
+                            int rows, void *dst, int T, int row_bytes,
+                            hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int V = row_bytes / 16;  // 16-byte vectors per row
+  const int need = (V + kWave - 1) / kWave;
+  if (need <= 1) return launch_vpl<1>(x, slots, dst, T, W, V, rows, stream);
+  if (need <= 2) return launch_vpl<2>(x, slots, dst, T, W, V, rows, stream);
+  if (need <= 4) return launch_vpl<4>(x, slots, dst, T, W, V, rows, stream);
+  if (need <= 8) return launch_vpl<8>(x, slots, dst, T, W, V, rows, stream);
+  return launch_vpl<16>(x, slots, dst, T, W, V, rows, stream);
+}
+
 hipError_t launch_pack(const moe_cfg &c, const void *x,
                        const int32_t *slot_pos, void *send,
                        hipStream_t stream) {
-  if (c.T == 0) return hipSuccess;
   const int b = c.x_dtype == MOE_F32 ? 4 : 2;
-  const int V = (int)((size_t)c.H * b / 16);  // 16-byte vectors per row
-  const int need = (V + kWave - 1) / kWave;
-  if (need <= 1) return launch_vpl<1>(x, slot_pos, send, c.T, c.K, V, stream);
-  if (need <= 2) return launch_vpl<2>(x, slot_pos, send, c.T, c.K, V, stream);
-  if (need <= 4) return launch_vpl<4>(x, slot_pos, send, c.T, c.K, V, stream);
-  if (need <= 8) return launch_vpl<8>(x, slot_pos, send, c.T, c.K, V, stream);
-  return launch_vpl<16>(x, slot_pos, send, c.T, c.K, V, stream);
+  return launch_pack_rows(x, slot_pos, c.K, c.T * c.K, send, c.T, c.H * b,
+                          stream);
 }
 
 }  // namespace moe

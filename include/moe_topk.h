@@ -195,6 +195,69 @@ int moe_dispatch_combine(const moe_cfg *cfg, const void *x,
                          const moe_layout *layout, void *send, void *out,
                          void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- node-level two-leg dispatch and hierarchical combine -------------
+ * "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+ * Training", Section 1: a token whose experts share a node crosses to that
+ * node once and is forwarded inside it.  "MoX: Efficient MoE Routing on
+ * Direct-Connect Topologies", Section 2.5: on the way back a node reduces
+ * the expert outputs it holds for a token and forwards one vector.
+ * The leg-1 buffer node_send and the partial buffer part have
+ * moe_node_rows_max(cfg) = T * min(K, N) rows of H elements; the rows in
+ * use are [0, node_off[N]), node-major with tokens ascending (node_slot from
+ * moe_dispatch_layout).  node(e) = (e / (E/R)) / (R/N). */
+
+/* Rows of the node_send and part buffers for cfg (0 when cfg is invalid).
+ * Host only. */
+size_t moe_node_rows_max(const moe_cfg *cfg);
+
+/* Leg 1: node_send[node_slot[t*N+n]] = x[t] (x_dtype rows, bit for bit)
+ * for every (t, n) with node_slot >= 0.  node_slot [T*N] int32 as produced
+ * by moe_dispatch_layout; entries outside [0, moe_node_rows_max) skipped. */
+int moe_dispatch_pack_nodes(const moe_cfg *cfg, const void *x,
+                            const int32_t *node_slot, void *node_send,
+                            hipStream_t stream);
+
+/* Leg 2: send[slot_pos[t*K+k]] = node_send[node_slot[t*N + node(e)]] with
+ * e = topk_idx[t*K+k]: the row that reached expert e's node is forwarded to
+ * the expert's segment.  With node_send from moe_dispatch_pack_nodes, send
+ * equals what moe_dispatch_pack writes.  Slots with an expert id outside
+ * [0, E), a send row outside [0, T*K) or no node row are skipped. */
+int moe_dispatch_forward(const moe_cfg *cfg, const void *node_send,
+                         const int32_t *node_slot, const int32_t *topk_idx,
+                         const int32_t *slot_pos, void *send,
+                         hipStream_t stream);
+
+/* Reverse of leg 2, per node: for every (t, n) with node_slot >= 0,
+ *   part[node_slot[t*N+n]] = sum over k with node(e(t,k)) == n of
+ *                            w[t,k] * s[e(t,k)] * y[slot_pos[t,k]]
+ * accumulated in fp32 and rounded to nearest-even once into part_dtype
+ * (MOE_F32 or MOE_BF16).  y, slot_pos, topk_w, expert_scale as in
+ * moe_combine; topk_idx is required (it places each slot on a node). */
+int moe_combine_partial(const moe_cfg *cfg, const void *y,
+                        const int32_t *slot_pos, const float *topk_w,
+                        const int32_t *topk_idx, const float *expert_scale,
+                        const int32_t *node_slot, int32_t part_dtype,
+                        void *part, hipStream_t stream);
+
+/* Reverse of leg 1, at the source: out[t] = sum over n with node_slot >= 0
+ * of part[node_slot[t*N+n]], accumulated in fp32 and rounded once into
+ * out_dtype. */
+int moe_combine_nodes(const moe_cfg *cfg, const void *part,
+                      int32_t part_dtype, const int32_t *node_slot, void *out,
+                      hipStream_t stream);
+
+/* The two-leg path: gate -> layout (layout->node_slot required) -> leg 1 ->
+ * leg 2 -> per-node partials of the stand-in expert applied to send ->
+ * sum at the source.  Outputs as in the calls above; out is computed from
+ * the partials, never from x. */
+int moe_dispatch_combine_nodes(const moe_cfg *cfg, const void *x,
+                               const float *logits, const float *expert_scale,
+                               int32_t *topk_idx, float *topk_w,
+                               const moe_layout *layout, void *node_send,
+                               void *send, int32_t part_dtype, void *part,
+                               void *out, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* Copy the workspace error word (MOE_DEVERR_* bits, 0 when clean) to
  * *host_code after all work queued on `stream`; synchronises `stream`.  When
  * `clear` is non-zero the word is reset to 0 afterwards (enqueued). */

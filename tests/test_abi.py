@@ -123,3 +123,31 @@ def test_host_validation_before_any_device_work():
                                    None, 0, None) == moe.MOE_EINVAL
     assert lib.moe_workspace_init(None, 0, None) == moe.MOE_EWORKSPACE
     assert lib.moe_read_device_error(None, None, None, 0) == moe.MOE_EINVAL
+
+
+def test_node_entry_points_declared_and_validated():
+    names = declared_functions()
+    for n in ("moe_node_rows_max", "moe_dispatch_pack_nodes",
+              "moe_dispatch_forward", "moe_combine_partial",
+              "moe_combine_nodes", "moe_dispatch_combine_nodes"):
+        assert n in names
+    c = cfg()
+    assert moe.moe_node_rows_max(c) == 16384 * 8          # T * min(K, N)
+    assert moe.moe_node_rows_max(cfg(K=2, N=1, R=8, E=8)) == 16384
+    assert moe.moe_node_rows_max(cfg(E=250)) == 0
+    lib = moe.lib()
+    assert lib.moe_dispatch_pack_nodes(ctypes.byref(c), None, None, None,
+                                       None) == moe.MOE_EINVAL
+    assert lib.moe_dispatch_forward(ctypes.byref(c), None, None, None, None,
+                                    None, None) == moe.MOE_EINVAL
+    # a partial type other than f32/bf16 is refused before any pointer check
+    assert lib.moe_combine_partial(ctypes.byref(c), None, None, None, None,
+                                   None, None, 5, None, None) == moe.MOE_EUNSUPPORTED
+    assert lib.moe_combine_nodes(ctypes.byref(c), None, 5, None, None,
+                                 None) == moe.MOE_EUNSUPPORTED
+    assert lib.moe_combine_nodes(ctypes.byref(c), None, moe.MOE_BF16, None,
+                                 None, None) == moe.MOE_EINVAL
+    lay = moe.moe_layout()
+    assert lib.moe_dispatch_combine_nodes(
+        ctypes.byref(c), None, None, None, None, None, ctypes.byref(lay),
+        None, None, moe.MOE_BF16, None, None, None, 0, None) == moe.MOE_EINVAL
