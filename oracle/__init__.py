@@ -11,8 +11,9 @@ deduplication and the OCS decode paper's "Variable MoE Traffic and
 Regularization" for per-destination row counts; pack and combine: the same
 blog's "Envío (Dispatch)" and "Combinación (Combine)" sections; the two-leg
 node-level dispatch and the per-node partial combine: Cobalt Section 1 and
-"MoX: Efficient MoE Routing on Direct-Connect Topologies" Section 2.5).  All
-are pinned by the CPU tests.
+"MoX: Efficient MoE Routing on Direct-Connect Topologies" Section 2.5; the
+FP8 dispatch with block scales: the blog's "Envío (Dispatch)" and the OCS
+decode paper's "Communication precision").  All are pinned by the CPU tests.
 """
 from __future__ import annotations
 
@@ -61,6 +62,17 @@ def _lib() -> ctypes.CDLL:
         lib.moe_ref_combine_nodes.argtypes = (
             [ctypes.c_int] * 4 + [_P, ctypes.c_int, _P, ctypes.c_int, _P,
                                   _P])
+        lib.moe_ref_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.moe_ref_e4m3_value.restype = ctypes.c_double
+        lib.moe_ref_e4m3_code.argtypes = [ctypes.c_double]
+        lib.moe_ref_e4m3_code.restype = ctypes.c_uint8
+        lib.moe_ref_fp8_row_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.moe_ref_fp8_row_bytes.restype = ctypes.c_size_t
+        lib.moe_ref_pack_fp8.argtypes = [ctypes.c_int] * 5 + [_P] * 3
+        lib.moe_ref_combine_fp8.argtypes = ([ctypes.c_int] * 4 + [_P] * 5 +
+                                            [ctypes.c_int, _P, _P])
+        for f in ("moe_ref_pack_fp8", "moe_ref_combine_fp8"):
+            getattr(lib, f).restype = ctypes.c_int
         for f in ("moe_ref_gate", "moe_ref_layout", "moe_ref_pack",
                   "moe_ref_combine", "moe_ref_combine_tokens",
                   "moe_ref_pack_nodes", "moe_ref_forward",
@@ -300,6 +312,86 @@ def dispatch_combine_nodes(x: np.ndarray, logits: np.ndarray, K: int, R: int,
     res.update(topk_idx=idx, topk_w=w, node_send=node_send, send=send,
                part=part, part_exact=part_exact, out=out,
                out_exact=out_exact)
+    return res
+
+
+# ---- FP8 dispatch with per-block scales ------------------------------------
+
+def e4m3_value(codes) -> np.ndarray:
+    """Exact values of E4M3 codes (uint8) as fp64."""
+    f = _lib().moe_ref_e4m3_value
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([f(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def e4m3_code(values) -> np.ndarray:
+    """E4M3 codes of fp64 values (magnitude clamped to 448, ties to even)."""
+    f = _lib().moe_ref_e4m3_code
+    v = np.asarray(values, dtype=np.float64)
+    return np.array([f(float(a)) for a in v.ravel()],
+                    dtype=np.uint8).reshape(v.shape)
+
+
+def fp8_row_bytes(H: int, B: int) -> int:
+    return int(_lib().moe_ref_fp8_row_bytes(H, B))
+
+
+def pack_fp8(x: np.ndarray, slot_pos: np.ndarray, B: int = 128) -> np.ndarray:
+    """Quantise each token's row once and write it to its K send rows.
+
+    Returns send as uint8 [T*K, H + 4*H/B]: H E4M3 codes then H/B fp32
+    scales per row.
+    """
+    x = np.ascontiguousarray(x)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    T, K = slot_pos.shape
+    H = x.shape[1]
+    send = np.zeros((T * K, fp8_row_bytes(H, B)), np.uint8)
+    _check(_lib().moe_ref_pack_fp8(T, K, H, B, _dtype_code(x), _ptr(x),
+                                   _ptr(slot_pos), _ptr(send)), "pack_fp8")
+    return send
+
+
+def fp8_rows_split(send: np.ndarray, H: int, B: int = 128):
+    """(codes uint8 [rows, H], scales fp32 [rows, H/B]) of an FP8 buffer."""
+    send = np.ascontiguousarray(send)
+    return send[:, :H], send[:, H:].copy().view(np.float32)
+
+
+def combine_fp8(y: np.ndarray, slot_pos: np.ndarray, topk_w: np.ndarray,
+                H: int, B: int = 128, topk_idx: Optional[np.ndarray] = None,
+                expert_scale: Optional[np.ndarray] = None,
+                out_dtype: str = "bf16"):
+    """Weighted sum of dequantised FP8 rows: ``(out, exact)``."""
+    y = np.ascontiguousarray(y, dtype=np.uint8)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    T, K = slot_pos.shape
+    if expert_scale is not None:
+        expert_scale = np.ascontiguousarray(expert_scale, dtype=np.float32)
+        topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    ocode = DT_F32 if out_dtype == "f32" else DT_BF16
+    out = np.empty((T, H), np.float32 if ocode == DT_F32 else np.uint16)
+    exact = np.empty((T, H), np.float64)
+    _check(_lib().moe_ref_combine_fp8(
+        T, H, K, B, _ptr(y), _ptr(slot_pos), _ptr(topk_w), _ptr(topk_idx),
+        _ptr(expert_scale), ocode, _ptr(out), _ptr(exact)), "combine_fp8")
+    return out, exact
+
+
+def dispatch_combine_fp8(x: np.ndarray, logits: np.ndarray, K: int, R: int,
+                         N: int, expert_scale: Optional[np.ndarray] = None,
+                         out_dtype: str = "bf16", B: int = 128,
+                         renorm: bool = True) -> dict:
+    """gate -> layout -> quantising pack -> combine of the FP8 rows."""
+    idx, w = gate(logits, K, renorm)
+    E = logits.shape[1]
+    lay = layout(idx, E, R, N)
+    send = pack_fp8(x, lay["slot_pos"], B)
+    out, exact = combine_fp8(send, lay["slot_pos"], w, x.shape[1], B, idx,
+                             expert_scale, out_dtype)
+    res = dict(lay)
+    res.update(topk_idx=idx, topk_w=w, send=send, out=out, out_exact=exact)
     return res
 
 

@@ -478,3 +478,158 @@ int moe_ref_combine_nodes(int T, int H, int N, int part_dtype,
   }
   return REF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 6. FP8 dispatch with per-block scales                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * "Efficient and portable mixture-of-experts communication", sections
+ * "Envío (Dispatch)" and "Combinación (Combine)": the dispatch sends tokens
+ * with block scale factors (a quantised payload), the combine sends 16-bit
+ * activations and forms the weighted average.  "Workload-Static Optical
+ * Circuit Switching for Scalable LLM Inference Decode", section
+ * "Communication precision": FP8 is supported for MoE dispatch.  The pages
+ * name neither the 8-bit format nor the block size; the readings taken here:
+ *   - codes are OCP FP8 E4M3: 1 sign bit, 4 exponent bits with bias 7, 3
+ *     mantissa bits, subnormals below 2^-6, no infinities, largest finite
+ *     magnitude 448 (exponent 15 with mantissa 7 is NaN); round to nearest,
+ *     ties to even; the sign of the input is kept (also on zero);
+ *   - every block of B consecutive elements of a row has one fp32 scale
+ *     s = amax / 448 (amax = largest magnitude in the block), and its codes
+ *     are e4m3(x * r) with r = 448 / amax; both quotients and the product
+ *     are fp32 operations (round to nearest-even), so the integer codes are
+ *     decided in the precision the kernel uses; a block of zeros has s = 0
+ *     and zero codes;
+ *   - a packed row is H code bytes followed by the H/B scales (fp32, little
+ *     endian): H + 4H/B bytes;
+ *   - dequantised value = code value * s.
+ */
+
+/* Value of an E4M3 code (exact; NaN codes return NaN). */
+double moe_ref_e4m3_value(uint8_t c) {
+  int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
+  if (ex == 15 && man == 7) return NAN;
+  double mag = ex == 0 ? ldexp((double)man, -9)          /* man/8 * 2^-6 */
+                       : ldexp(8.0 + man, ex - 7 - 3);   /* (1+man/8) 2^(ex-7) */
+  return sign ? -mag : mag;
+}
+
+/* E4M3 code of v: magnitude clamped to 448, then rounded to the nearest
+ * representable value with ties to the even mantissa. */
+uint8_t moe_ref_e4m3_code(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  if (a > 448.0) a = 448.0;
+  uint8_t code;
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: multiples of 2^-9; 2^-6 itself is the first normal */
+    double m = nearbyint(ldexp(a, 9)); /* 0..8, ties to even */
+    code = (uint8_t)m;                 /* m == 8 encodes 2^-6 (exp 1, man 0) */
+  } else {
+    int e;
+    (void)frexp(a, &e);                /* a = f 2^e, 0.5 <= f < 1 */
+    e -= 1;                            /* a in [2^e, 2^(e+1)) */
+    double m = nearbyint(ldexp(a, 3 - e)); /* 8..16, ties to even */
+    if (m == 16.0) {
+      m = 8.0;
+      e += 1;
+    }
+    code = (uint8_t)(((e + 7) << 3) | ((int)m - 8));
+  }
+  return (uint8_t)(code | (neg << 7));
+}
+
+static float row_value_f32(int dtype, const void *rows, size_t at) {
+  if (dtype == REF_DT_F32) return ((const float *)rows)[at];
+  uint32_t u = (uint32_t)((const uint16_t *)rows)[at] << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* Quantise one row of H elements (x_dtype) into codes[H] and scales[H/B]. */
+static void quant_row(int H, int B, int x_dtype, const void *x, size_t row,
+                      uint8_t *codes, float *scales) {
+  for (int b0 = 0; b0 < H; b0 += B) {
+    float amax = 0.0f;
+    for (int i = b0; i < b0 + B; ++i) {
+      float v = fabsf(row_value_f32(x_dtype, x, row * H + i));
+      if (v > amax) amax = v;
+    }
+    volatile float s = amax / 448.0f; /* fp32 quotient */
+    scales[b0 / B] = s;
+    if (amax == 0.0f) {
+      for (int i = b0; i < b0 + B; ++i)
+        codes[i] = signbit(row_value_f32(x_dtype, x, row * H + i)) ? 0x80 : 0;
+      continue;
+    }
+    volatile float r = 448.0f / amax; /* fp32 quotient */
+    for (int i = b0; i < b0 + B; ++i) {
+      volatile float p = row_value_f32(x_dtype, x, row * H + i) * r;
+      codes[i] = moe_ref_e4m3_code((double)p);
+    }
+  }
+}
+
+/* Row bytes of the FP8 send buffer: H codes + H/B fp32 scales. */
+size_t moe_ref_fp8_row_bytes(int H, int B) {
+  return (size_t)H + 4 * (size_t)(H / B);
+}
+
+/* Pack with quantisation: every token's row is quantised once and written
+ * to its K send rows: send[slot_pos[t*K+k]] = codes(x[t]) | scales(x[t]). */
+int moe_ref_pack_fp8(int T, int K, int H, int B, int x_dtype, const void *x,
+                     const int32_t *slot_pos, void *send) {
+  if (T < 0 || K < 1 || H < 1 || B < 1 || H % B != 0) return REF_EINVAL;
+  const size_t rb = moe_ref_fp8_row_bytes(H, B);
+  unsigned char *dst = (unsigned char *)send;
+  uint8_t codes[65536];
+  float scales[65536];
+  if (H > 65536) return REF_EINVAL;
+  for (int t = 0; t < T; ++t) {
+    quant_row(H, B, x_dtype, x, (size_t)t, codes, scales);
+    for (int k = 0; k < K; ++k) {
+      int32_t s = slot_pos[(size_t)t * K + k];
+      if (s < 0 || (size_t)s >= (size_t)T * K) return REF_EINVAL;
+      unsigned char *row = dst + (size_t)s * rb;
+      memcpy(row, codes, (size_t)H);
+      memcpy(row + H, scales, sizeof(float) * (size_t)(H / B));
+    }
+  }
+  return REF_OK;
+}
+
+/* Dequantised value of element h of an FP8 row. */
+static double fp8_row_value(const unsigned char *row, int H, int B, int h) {
+  float s;
+  memcpy(&s, row + H + 4 * (size_t)(h / B), sizeof s);
+  return moe_ref_e4m3_value(row[h]) * (double)s;
+}
+
+/* Combine of FP8 rows: out[t,h] = sum_k w[t,k] s[e(t,k)] deq(y[slot_pos[t,k]], h)
+ * in fp64, k order; out_exact (may be NULL) unrounded, out (may be NULL)
+ * rounded to nearest-even in out_dtype. */
+int moe_ref_combine_fp8(int T, int H, int K, int B, const void *y,
+                        const int32_t *slot_pos, const float *topk_w,
+                        const int32_t *topk_idx, const float *expert_scale,
+                        int out_dtype, void *out, double *out_exact) {
+  if (T < 0 || H < 1 || K < 1 || B < 1 || H % B != 0) return REF_EINVAL;
+  if (expert_scale && !topk_idx) return REF_EINVAL;
+  const size_t rb = moe_ref_fp8_row_bytes(H, B);
+  const unsigned char *src = (const unsigned char *)y;
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) {
+        size_t i = (size_t)t * K + k;
+        double c = (double)topk_w[i];
+        if (expert_scale) c *= (double)expert_scale[topk_idx[i]];
+        acc += c * fp8_row_value(src + (size_t)slot_pos[i] * rb, H, B, h);
+      }
+      size_t o = (size_t)t * H + h;
+      if (out_exact) out_exact[o] = acc;
+      if (out) store_value(out_dtype, out, o, acc);
+    }
+  }
+  return REF_OK;
+}
