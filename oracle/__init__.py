@@ -339,8 +339,8 @@ def fp8_row_bytes(H: int, B: int) -> int:
 def pack_fp8(x: np.ndarray, slot_pos: np.ndarray, B: int = 128) -> np.ndarray:
     """Quantise each token's row once and write it to its K send rows.
 
-    Returns send as uint8 [T*K, H + 4*H/B]: H E4M3 codes then H/B fp32
-    scales per row.
+    Returns send as uint8 [T*K, round_up(H + 4*H/B, 16)]: H E4M3 codes, then
+    H/B fp32 scales, then zero padding, per row.
     """
     x = np.ascontiguousarray(x)
     slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
@@ -355,7 +355,7 @@ def pack_fp8(x: np.ndarray, slot_pos: np.ndarray, B: int = 128) -> np.ndarray:
 def fp8_rows_split(send: np.ndarray, H: int, B: int = 128):
     """(codes uint8 [rows, H], scales fp32 [rows, H/B]) of an FP8 buffer."""
     send = np.ascontiguousarray(send)
-    return send[:, :H], send[:, H:].copy().view(np.float32)
+    return send[:, :H], send[:, H:H + 4 * (H // B)].copy().view(np.float32)
 
 
 def combine_fp8(y: np.ndarray, slot_pos: np.ndarray, topk_w: np.ndarray,

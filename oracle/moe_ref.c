@@ -501,7 +501,8 @@ int moe_ref_combine_nodes(int T, int H, int N, int part_dtype,
  *     decided in the precision the kernel uses; a block of zeros has s = 0
  *     and zero codes;
  *   - a packed row is H code bytes followed by the H/B scales (fp32, little
- *     endian): H + 4H/B bytes;
+ *     endian), zero-padded to a multiple of 16 bytes so that every row
+ *     starts on a 16-byte boundary: round_up(H + 4H/B, 16) bytes;
  *   - dequantised value = code value * s.
  */
 
@@ -571,9 +572,10 @@ static void quant_row(int H, int B, int x_dtype, const void *x, size_t row,
   }
 }
 
-/* Row bytes of the FP8 send buffer: H codes + H/B fp32 scales. */
+/* Row bytes of the FP8 send buffer: H codes + H/B fp32 scales, rounded up
+ * to a multiple of 16. */
 size_t moe_ref_fp8_row_bytes(int H, int B) {
-  return (size_t)H + 4 * (size_t)(H / B);
+  return ((size_t)H + 4 * (size_t)(H / B) + 15) & ~(size_t)15;
 }
 
 /* Pack with quantisation: every token's row is quantised once and written
@@ -592,6 +594,7 @@ int moe_ref_pack_fp8(int T, int K, int H, int B, int x_dtype, const void *x,
       int32_t s = slot_pos[(size_t)t * K + k];
       if (s < 0 || (size_t)s >= (size_t)T * K) return REF_EINVAL;
       unsigned char *row = dst + (size_t)s * rb;
+      memset(row, 0, rb);
       memcpy(row, codes, (size_t)H);
       memcpy(row + H, scales, sizeof(float) * (size_t)(H / B));
     }

@@ -122,7 +122,9 @@ def test_pack_fp8_equals_independent_quantisation(xdt, B):
     idx, _ = oracle.gate(d["logits"], w.K)
     lay = oracle.layout(idx, w.E, w.R, w.N)
     send = oracle.pack_fp8(x, lay["slot_pos"], B)
-    assert send.shape == (w.T * w.K, w.H + 4 * w.H // B)
+    rb = -(-(w.H + 4 * w.H // B) // 16) * 16
+    assert send.shape == (w.T * w.K, rb)
+    assert not send[:, w.H + 4 * w.H // B:].any()  # zero padding
     codes, scales = oracle.fp8_rows_split(send, w.H, B)
     xf = x if xdt == mi.F32 else mi.bf16_bits_to_f32(x)
     want_c, want_s = _numpy_quant(xf.astype(np.float32), B)
