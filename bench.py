@@ -10,12 +10,14 @@ sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload deepseek_v3] [--no-cpu-baseline]
-                       [--path flat|two_leg] [--part-dtype bf16|f32]
+                       [--path flat|two_leg|fp8] [--part-dtype bf16|f32]
 
 --path two_leg times moe_dispatch_combine_nodes instead: the node-level
 two-leg dispatch (one row per (token, node) crossing, then forwarded to the
 experts) and the hierarchical combine (per-node partial sums, then their sum
-at the source).
+at the source).  --path fp8 times moe_dispatch_combine_fp8: the pack
+quantises each row to E4M3 codes with one fp32 scale per 128 elements and the
+combine gathers and dequantises those rows.
 """
 from __future__ import annotations
 
@@ -122,7 +124,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--fused-only", action="store_true",
                     help="time only the fused call (for profiler runs)")
-    ap.add_argument("--path", default="flat", choices=("flat", "two_leg"))
+    ap.add_argument("--path", default="flat",
+                    choices=("flat", "two_leg", "fp8"))
     ap.add_argument("--part-dtype", default="bf16", choices=("bf16", "f32"))
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB "
@@ -169,6 +172,10 @@ def main() -> int:
     if args.path == "two_leg":
         return two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out,
                        ws, stream)
+    if args.path == "fp8":
+        del send
+        return fp8_path(args, w, cfg, x, lg, scale, idx, wt, lay, out, ws,
+                        stream)
 
     def step():
         moe.moe_dispatch_combine(cfg, x, lg, scale, idx, wt, lay, send, out,
@@ -352,6 +359,93 @@ def two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out, ws,
                 "frac_of_peak": gbps / HBM_PEAK_GBPS},
         "dedup": {"crossing_rows": D, "slot_rows": w.T * w.K,
                   "inter_node_row_ratio": D / (w.T * w.K)},
+        "steps_ms": steps_ms,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "alg_bytes_per_launch": kb[dom],
+                     "launch_ms": steps_ms[dom],
+                     **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
+                        for k in kb}},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def fp8_path(args, w, cfg, x, lg, scale, idx, wt, lay, out, ws,
+             stream) -> int:
+    """Time moe_dispatch_combine_fp8 (E4M3 rows, scale per 128); JSON line."""
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    B = 128
+    rb = moe.moe_fp8_row_bytes(w.H, B)
+    if rb == 0:
+        raise SystemExit(f"H={w.H} does not split into blocks of {B}")
+    send = torch.empty((w.T * w.K, rb), dtype=torch.uint8, device=x.device)
+
+    def step():
+        moe.moe_dispatch_combine_fp8(cfg, x, lg, scale, idx, wt, lay, send,
+                                     out, ws, B, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if moe.moe_read_device_error(ws) != 0:
+        raise RuntimeError("device reported an input error")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"bench: fp8 {ms:.4f} ms/step", file=sys.stderr, flush=True)
+
+    b, ob = w.elem_bytes, w.out_elem_bytes
+    T, H, K = w.T, w.H, w.K
+    kb = {"pack_fp8": T * H * b + T * K * rb + 4 * T * K,
+          "combine_fp8": T * K * rb + T * H * ob + 12 * T * K + 4 * w.E}
+    meta = T * (4 * w.E + 32 * K + 8) + 8 * (w.E + w.R + w.N)
+    alg = kb["pack_fp8"] + kb["combine_fp8"] + meta - 4 * T * K - 12 * T * K
+    n = max(args.steps, 5)
+    names = ("gate", "layout", "pack_fp8", "combine_fp8")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+           for _ in range(n)]
+    for i in range(n):
+        e = evs[i]
+        e[0].record(stream)
+        moe.moe_topk_gate(cfg, lg, idx, wt, stream)
+        e[1].record(stream)
+        moe.moe_dispatch_layout(cfg, idx, lay, ws, stream)
+        e[2].record(stream)
+        moe.moe_dispatch_pack_fp8(cfg, x, lay.slot_pos, send, B, stream)
+        e[3].record(stream)
+        moe.moe_combine_fp8(cfg, send, lay.slot_pos, wt, idx, scale, out, B,
+                            stream)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    steps_ms = {nm: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                   for i in range(n)]))
+                for j, nm in enumerate(names)}
+    dom = max(kb, key=lambda k: steps_ms[k])
+    achieved = kb[dom] / (steps_ms[dom] * 1e-3) / 1e9
+    gbps = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8-e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "path": "fp8", "T": T, "H": H,
+                   "E": w.E, "K": K, "R": w.R, "N": w.N, "rows": w.x_dtype,
+                   "payload": "e4m3+f32 scale/128", "accumulate": "f32",
+                   "seed": w.seed},
+        "hbm": {"alg_bytes": alg, "gbps": gbps,
+                "frac_of_peak": gbps / HBM_PEAK_GBPS},
         "steps_ms": steps_ms,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

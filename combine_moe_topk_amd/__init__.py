@@ -6,7 +6,9 @@ match the C entry points: :func:`moe_topk_gate`, :func:`moe_dispatch_layout`,
 :func:`moe_dispatch_pack`, :func:`moe_combine`, :func:`moe_dispatch_combine`,
 and the node-level two-leg path :func:`moe_dispatch_pack_nodes`,
 :func:`moe_dispatch_forward`, :func:`moe_combine_partial`,
-:func:`moe_combine_nodes`, :func:`moe_dispatch_combine_nodes`.
+:func:`moe_combine_nodes`, :func:`moe_dispatch_combine_nodes`, and the FP8
+dispatch :func:`moe_dispatch_pack_fp8`, :func:`moe_combine_fp8`,
+:func:`moe_dispatch_combine_fp8`.
 """
 from ._lib import (  # noqa: F401
     LAYOUT_FIELDS, Layout, MoeError, MOE_BF16, MOE_DEVERR_DUP_EXPERT,
@@ -18,4 +20,6 @@ from ._lib import (  # noqa: F401
     moe_validate_cfg, moe_version, moe_workspace_bytes, moe_workspace_init,
     moe_node_rows_max, moe_dispatch_pack_nodes, moe_dispatch_forward,
     moe_combine_partial, moe_combine_nodes, moe_dispatch_combine_nodes,
+    moe_fp8_row_bytes, moe_dispatch_pack_fp8, moe_combine_fp8,
+    moe_dispatch_combine_fp8,
 )

@@ -96,6 +96,15 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_combine_nodes": (ctypes.c_int, [
                 _CFG, _P, _P, _P, _P, _P, _LAY, _P, _P, ctypes.c_int32, _P,
                 _P, _P, ctypes.c_size_t, _P]),
+            "moe_fp8_row_bytes": (ctypes.c_size_t, [ctypes.c_int32,
+                                                    ctypes.c_int32]),
+            "moe_dispatch_pack_fp8": (ctypes.c_int, [_CFG, _P, _P,
+                                                     ctypes.c_int32, _P, _P]),
+            "moe_combine_fp8": (ctypes.c_int, [_CFG, _P, ctypes.c_int32, _P,
+                                               _P, _P, _P, _P, _P]),
+            "moe_dispatch_combine_fp8": (ctypes.c_int, [
+                _CFG, _P, _P, _P, _P, _P, _LAY, ctypes.c_int32, _P, _P, _P,
+                ctypes.c_size_t, _P]),
             "moe_read_device_error": (ctypes.c_int, [_P, _P,
                                                      ctypes.POINTER(ctypes.c_int32),
                                                      ctypes.c_int]),
@@ -364,6 +373,57 @@ def moe_dispatch_combine_nodes(cfg: moe_cfg, x: torch.Tensor,
         _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
         "moe_dispatch_combine_nodes")
+
+
+# ---- FP8 dispatch with per-block scales -----------------------------------
+
+def moe_fp8_row_bytes(H: int, qblock: int = 128) -> int:
+    """Stride of a packed FP8 row (codes, scales, padding); 0 if unsupported."""
+    return lib().moe_fp8_row_bytes(H, qblock)
+
+
+def moe_dispatch_pack_fp8(cfg: moe_cfg, x: torch.Tensor,
+                          slot_pos: torch.Tensor, send: torch.Tensor,
+                          qblock: int = 128, stream=None) -> None:
+    _check(lib().moe_dispatch_pack_fp8(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(slot_pos, torch.int32, "slot_pos"), qblock,
+        _ptr(send, torch.uint8, "send"), _stream(stream)),
+        "moe_dispatch_pack_fp8")
+
+
+def moe_combine_fp8(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
+                    topk_w: torch.Tensor, topk_idx: Optional[torch.Tensor],
+                    expert_scale: Optional[torch.Tensor], out: torch.Tensor,
+                    qblock: int = 128, stream=None) -> None:
+    _check(lib().moe_combine_fp8(
+        ctypes.byref(cfg), _ptr(y, torch.uint8, "y"), qblock,
+        _ptr(slot_pos, torch.int32, "slot_pos"),
+        _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"), _stream(stream)),
+        "moe_combine_fp8")
+
+
+def moe_dispatch_combine_fp8(cfg: moe_cfg, x: torch.Tensor,
+                             logits: torch.Tensor,
+                             expert_scale: Optional[torch.Tensor],
+                             topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                             layout: Layout, send: torch.Tensor,
+                             out: torch.Tensor, ws: torch.Tensor,
+                             qblock: int = 128, stream=None) -> None:
+    lay = layout.c_struct()
+    _check(lib().moe_dispatch_combine_fp8(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(lay), qblock,
+        _ptr(send, torch.uint8, "send"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+        "moe_dispatch_combine_fp8")
 
 
 def moe_read_device_error(ws: torch.Tensor, clear: bool = True,

@@ -262,6 +262,70 @@ int moe_dispatch_combine_nodes(const moe_cfg *cfg, const void *x,
   return launch_status(e);
 }
 
+size_t moe_fp8_row_bytes(int32_t H, int32_t qblock) {
+  if (H < 1 || (qblock != 32 && qblock != 64 && qblock != 128) ||
+      H % qblock != 0 || H % 16 != 0)
+    return 0;
+  return moe::fp8_row_bytes(H, qblock);
+}
+
+int moe_dispatch_pack_fp8(const moe_cfg *cfg, const void *x,
+                          const int32_t *slot_pos, int32_t qblock, void *send,
+                          hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!moe::fp8_block_ok(*cfg, qblock)) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !slot_pos || !send) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(send) || !aligned(slot_pos, 4))
+    return MOE_EUNSUPPORTED;
+  return launch_status(
+      moe::launch_pack_fp8(*cfg, qblock, x, slot_pos, send, stream));
+}
+
+int moe_combine_fp8(const moe_cfg *cfg, const void *y, int32_t qblock,
+                    const int32_t *slot_pos, const float *topk_w,
+                    const int32_t *topk_idx, const float *expert_scale,
+                    void *out, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!moe::fp8_block_ok(*cfg, qblock)) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y || !slot_pos || !topk_w || !out) return MOE_EINVAL;
+  if (expert_scale && !topk_idx) return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(out)) return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_combine_fp8(*cfg, qblock, y, slot_pos,
+                                               topk_w, topk_idx, expert_scale,
+                                               out, stream));
+}
+
+int moe_dispatch_combine_fp8(const moe_cfg *cfg, const void *x,
+                             const float *logits, const float *expert_scale,
+                             int32_t *topk_idx, float *topk_w,
+                             const moe_layout *layout, int32_t qblock,
+                             void *send, void *out, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!moe::fp8_block_ok(*cfg, qblock)) return MOE_EUNSUPPORTED;
+  if ((rc = check_layout_ptrs(cfg, layout)) != MOE_OK) return rc;
+  if ((rc = check_ws(cfg, ws, ws_bytes)) != MOE_OK) return rc;
+  if (cfg->T > 0) {
+    if (!x || !logits || !topk_idx || !topk_w || !send || !out)
+      return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(send) || !aligned16(out))
+      return MOE_EUNSUPPORTED;
+  }
+  hipError_t e = moe::launch_gate(*cfg, logits, topk_idx, topk_w, stream);
+  if (e == hipSuccess) e = moe::launch_layout(*cfg, topk_idx, *layout, ws, stream);
+  if (e == hipSuccess)
+    e = moe::launch_pack_fp8(*cfg, qblock, x, layout->slot_pos, send, stream);
+  if (e == hipSuccess)
+    e = moe::launch_combine_fp8(*cfg, qblock, send, layout->slot_pos, topk_w,
+                                topk_idx, expert_scale, out, stream);
+  return launch_status(e);
+}
+
 int moe_read_device_error(const void *ws, hipStream_t stream,
                           int32_t *host_code, int clear) {
   if (!ws || !host_code) return MOE_EINVAL;

@@ -1,0 +1,335 @@
+// FP8 (E4M3) dispatch with per-block scales, and the combine of FP8 rows,
+// for gfx950.
+//
+// "Efficient and portable mixture-of-experts communication", section
+// "Envío (Dispatch)": tokens are sent with block scale factors; "Workload-
+// Static Optical Circuit Switching for Scalable LLM Inference Decode",
+// section "Communication precision": FP8 transport for MoE dispatch.  The
+// format and block size are readings: OCP E4M3 codes (gfx950's native FP8
+// conversions), one fp32 scale s = amax/448 per block of B elements, codes
+// of fp32(x * fp32(448/amax)) clamped to +-448.  A packed row is H codes,
+// then H/B scales, then zero padding to a multiple of 16 bytes.
+//
+// Pack: one wave per token.  A lane holds 8 consecutive elements of the row
+// (one 16-byte bf16 vector); the B/8 lanes of a block reduce its amax with
+// xor-shuffles, every lane converts its 8 elements with v_cvt_pk_fp8_f32 and
+// the wave stores the codes (8 bytes a lane) and the block scales to the K
+// destination rows.  The row is read once and quantised once per token.
+//
+// Combine: as the bf16 combine, with 16 codes (one 16-byte vector) and their
+// block scale per unit; codes are widened with v_cvt_pk_f32_fp8 and
+// accumulated as fmaf(w * s_e * scale, code, acc) in fp32.
+#include "moe_internal.h"
+#include "row_io.h"
+
+namespace moe {
+namespace {
+
+// E4M3 codes of 4 fp32 values, packed little-endian in one word.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c,
+                                           float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// L = B/8 lanes per block; VPL units of 8 elements per lane and pass.
+template <bool XB, int L, int VPL>
+__global__ __launch_bounds__(256) void pack_fp8_kernel(
+    const char *__restrict__ x, const int32_t *__restrict__ slot_pos,
+    char *__restrict__ send, int T, int K, int U, int H, int rb, int rows) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // one token per wave: uniform exit
+  const int my_slot = lane < K ? slot_pos[(size_t)t * K + lane] : -1;
+  const char *xrow = x + (size_t)t * U * (XB ? 16 : 32);
+
+  for (int base = 0; base < U; base += kWave * VPL) {
+    Unit<XB> u[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      u[j].load(xrow, min(base + j * kWave + lane, U - 1));
+    uint32_t c0[VPL], c1[VPL];
+    float sc[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(u[j].get(e)));
+      // U is a multiple of L and every pass starts at a multiple of 64, so
+      // the L lanes of a block are aligned; lanes past the row end form
+      // whole blocks of their own and are never stored
+#pragma unroll
+      for (int off = 1; off < L; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+      sc[j] = a / 448.0f;
+      const float r = 448.0f / a;
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = u[j].get(e);
+        // a block of zeros keeps its zeros (and their signs)
+        p[e] = a == 0.0f ? v : fminf(fmaxf(v * r, -448.0f), 448.0f);
+      }
+      c0[j] = e4m3x4(p[0], p[1], p[2], p[3]);
+      c1[j] = e4m3x4(p[4], p[5], p[6], p[7]);
+    }
+    for (int k = 0; k < K; ++k) {
+      const int s = __builtin_amdgcn_readlane(my_slot, k);
+      if ((unsigned)s >= (unsigned)rows) continue;  // out-of-range: skipped
+      char *dst = send + (size_t)s * rb;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const int i = base + j * kWave + lane;
+        if (i < U) {
+          uint32_t *cw = (uint32_t *)(dst + (size_t)i * 8);
+          cw[0] = c0[j];
+          cw[1] = c1[j];
+          if (lane % L == 0) *(float *)(dst + H + 4 * (i / L)) = sc[j];
+        }
+      }
+    }
+  }
+}
+
+// Zero the padding words of every used send row once: a row is rb bytes, of
+// which [H + 4H/B, rb) are padding (at most 12 bytes).
+__global__ void pad_fp8_kernel(const int32_t *__restrict__ slot_pos,
+                               char *__restrict__ send, int n, int used,
+                               int rb, int rows) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int s = slot_pos[i];
+  if ((unsigned)s >= (unsigned)rows) return;
+  for (int b = used; b < rb; b += 4)
+    *(uint32_t *)(send + (size_t)s * rb + b) = 0u;
+}
+
+// 16 elements of a unit as fp32 from one 16-byte code vector.
+__device__ __forceinline__ void deq16(const u32x4 &q, float *f) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[w], true);
+    f[4 * w + 0] = lo[0];
+    f[4 * w + 1] = lo[1];
+    f[4 * w + 2] = hi[0];
+    f[4 * w + 3] = hi[1];
+  }
+}
+
+// KT > 0: compile-time K; KT == 0: runtime K.  UPT units of 16 codes per
+// thread and pass; L16 = B/16 units per block.  Row loads are branch-free
+// (clamped to the last unit) as in the bf16 combine.
+template <bool OB, int KT, int UPT, int TPT>
+__global__ __launch_bounds__(256) void combine_fp8_kernel(
+    const char *__restrict__ y, const int32_t *__restrict__ slot_pos,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ scale, char *__restrict__ out, int T, int Kr,
+    int U16, int H, int L16, int rb, int rows) {
+  const int K = KT > 0 ? KT : Kr;
+  const int lane = threadIdx.x % kWave;
+  const int tt = threadIdx.x % TPT;
+  const int t = blockIdx.x * (256 / TPT) + threadIdx.x / TPT;
+  if (t >= T) return;
+  int my_slot = 0;
+  float my_c = 0.0f;
+  if (lane < K) {
+    const size_t i = (size_t)t * K + lane;
+    my_slot = slot_pos[i];
+    my_c = topk_w[i];
+    if (scale) my_c *= scale[topk_idx[i]];
+    if ((unsigned)my_slot >= (unsigned)rows) {  // out of range: adds 0
+      my_slot = 0;
+      my_c = 0.0f;
+    }
+  }
+  char *orow = out + (size_t)t * H * (OB ? 2 : 4);
+
+  for (int base = 0; base < U16; base += TPT * UPT) {
+    float acc[UPT][16];
+#pragma unroll
+    for (int j = 0; j < UPT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+    if constexpr (KT > 0) {
+      u32x4 q[KT][UPT];
+      float bs[KT][UPT];
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const char *row =
+            y + (size_t)__builtin_amdgcn_readlane(my_slot, k) * rb;
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+          const int i = min(base + j * TPT + tt, U16 - 1);
+          q[k][j] = __builtin_nontemporal_load((const u32x4 *)row + i);
+          bs[k][j] = *(const float *)(row + H + 4 * (i / L16));
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const float c = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(my_c), k));
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+          float f[16];
+          deq16(q[k][j], f);
+          const float cs = c * bs[k][j];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[j][e] = fmaf(cs, f[e], acc[j][e]);
+        }
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const char *row =
+            y + (size_t)__builtin_amdgcn_readlane(my_slot, k) * rb;
+        const float c = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(my_c), k));
+        u32x4 q[UPT];
+        float bs[UPT];
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+          const int i = min(base + j * TPT + tt, U16 - 1);
+          q[j] = __builtin_nontemporal_load((const u32x4 *)row + i);
+          bs[j] = *(const float *)(row + H + 4 * (i / L16));
+        }
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+          float f[16];
+          deq16(q[j], f);
+          const float cs = c * bs[j];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[j][e] = fmaf(cs, f[e], acc[j][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int i = base + j * TPT + tt;
+      if (i < U16) {
+        store_unit<OB>(orow, 2 * i, acc[j]);
+        store_unit<OB>(orow, 2 * i + 1, acc[j] + 8);
+      }
+    }
+  }
+}
+
+template <bool XB, int L, int VPL>
+hipError_t launch_pack_v(const moe_cfg &c, const void *x,
+                         const int32_t *slot_pos, void *send, int rb,
+                         hipStream_t s) {
+  const int U = c.H / 8;
+  hipLaunchKernelGGL((pack_fp8_kernel<XB, L, VPL>), dim3((c.T + 3) / 4),
+                     dim3(256), 0, s, (const char *)x, slot_pos,
+                     (char *)send, c.T, c.K, U, c.H, rb, c.T * c.K);
+  return hipGetLastError();
+}
+
+template <bool XB, int L>
+hipError_t launch_pack_l(const moe_cfg &c, const void *x,
+                         const int32_t *slot_pos, void *send, int rb,
+                         hipStream_t s) {
+  const int need = (c.H / 8 + kWave - 1) / kWave;
+  if (need <= 1) return launch_pack_v<XB, L, 1>(c, x, slot_pos, send, rb, s);
+  if (need <= 2) return launch_pack_v<XB, L, 2>(c, x, slot_pos, send, rb, s);
+  if (need <= 4) return launch_pack_v<XB, L, 4>(c, x, slot_pos, send, rb, s);
+  if (need <= 8) return launch_pack_v<XB, L, 8>(c, x, slot_pos, send, rb, s);
+  return launch_pack_v<XB, L, 16>(c, x, slot_pos, send, rb, s);
+}
+
+template <bool XB>
+hipError_t launch_pack_b(const moe_cfg &c, int B, const void *x,
+                         const int32_t *slot_pos, void *send, int rb,
+                         hipStream_t s) {
+  switch (B) {
+    case 32: return launch_pack_l<XB, 4>(c, x, slot_pos, send, rb, s);
+    case 64: return launch_pack_l<XB, 8>(c, x, slot_pos, send, rb, s);
+    case 128: return launch_pack_l<XB, 16>(c, x, slot_pos, send, rb, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Units per thread: about 16 code loads (plus their scales) per thread.
+template <int KT>
+constexpr int fp8_upt() {
+  constexpr int kK = KT > 0 ? KT : 8;
+  constexpr int raw = 16 / kK;
+  return raw < 1 ? 1 : (raw > 8 ? 8 : raw);
+}
+
+template <bool OB, int KT>
+hipError_t launch_comb_k(const moe_cfg &c, int B, const void *y,
+                         const int32_t *slot_pos, const float *w,
+                         const int32_t *idx, const float *scale, void *out,
+                         int rb, hipStream_t s) {
+  constexpr int UPT = fp8_upt<KT>();
+  const int U16 = c.H / 16;
+  if (U16 <= 64 * UPT) {
+    hipLaunchKernelGGL((combine_fp8_kernel<OB, KT, UPT, 64>),
+                       dim3((c.T + 3) / 4), dim3(256), 0, s, (const char *)y,
+                       slot_pos, w, idx, scale, (char *)out, c.T, c.K, U16,
+                       c.H, B / 16, rb, c.T * c.K);
+  } else {
+    hipLaunchKernelGGL((combine_fp8_kernel<OB, KT, UPT, 256>), dim3(c.T),
+                       dim3(256), 0, s, (const char *)y, slot_pos, w, idx,
+                       scale, (char *)out, c.T, c.K, U16, c.H, B / 16, rb,
+                       c.T * c.K);
+  }
+  return hipGetLastError();
+}
+
+template <bool OB>
+hipError_t launch_comb_d(const moe_cfg &c, int B, const void *y,
+                         const int32_t *slot_pos, const float *w,
+                         const int32_t *idx, const float *scale, void *out,
+                         int rb, hipStream_t s) {
+  switch (c.K) {
+    case 1: return launch_comb_k<OB, 1>(c, B, y, slot_pos, w, idx, scale, out, rb, s);
+    case 2: return launch_comb_k<OB, 2>(c, B, y, slot_pos, w, idx, scale, out, rb, s);
+    case 4: return launch_comb_k<OB, 4>(c, B, y, slot_pos, w, idx, scale, out, rb, s);
+    case 8: return launch_comb_k<OB, 8>(c, B, y, slot_pos, w, idx, scale, out, rb, s);
+    case 16: return launch_comb_k<OB, 16>(c, B, y, slot_pos, w, idx, scale, out, rb, s);
+    default: return launch_comb_k<OB, 0>(c, B, y, slot_pos, w, idx, scale, out, rb, s);
+  }
+}
+
+}  // namespace
+
+size_t fp8_row_bytes(int H, int B) {
+  return ((size_t)H + 4 * (size_t)(H / B) + 15) & ~(size_t)15;
+}
+
+bool fp8_block_ok(const moe_cfg &c, int B) {
+  return (B == 32 || B == 64 || B == 128) && c.H % B == 0 && c.H % 16 == 0;
+}
+
+hipError_t launch_pack_fp8(const moe_cfg &c, int B, const void *x,
+                           const int32_t *slot_pos, void *send,
+                           hipStream_t stream) {
+  if (c.T == 0) return hipSuccess;
+  const int rb = (int)fp8_row_bytes(c.H, B);
+  const int used = c.H + 4 * (c.H / B);
+  hipError_t e = c.x_dtype == MOE_BF16
+                     ? launch_pack_b<true>(c, B, x, slot_pos, send, rb, stream)
+                     : launch_pack_b<false>(c, B, x, slot_pos, send, rb, stream);
+  if (e != hipSuccess || used == rb) return e;
+  const int n = c.T * c.K;
+  hipLaunchKernelGGL(pad_fp8_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     stream, slot_pos, (char *)send, n, used, rb, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_fp8(const moe_cfg &c, int B, const void *y,
+                              const int32_t *slot_pos, const float *topk_w,
+                              const int32_t *topk_idx,
+                              const float *expert_scale, void *out,
+                              hipStream_t stream) {
+  if (c.T == 0) return hipSuccess;
+  const int rb = (int)fp8_row_bytes(c.H, B);
+  if (c.out_dtype == MOE_BF16)
+    return launch_comb_d<true>(c, B, y, slot_pos, topk_w, topk_idx,
+                               expert_scale, out, rb, stream);
+  return launch_comb_d<false>(c, B, y, slot_pos, topk_w, topk_idx,
+                              expert_scale, out, rb, stream);
+}
+
+}  // namespace moe

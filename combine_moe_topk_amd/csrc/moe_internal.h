@@ -79,4 +79,19 @@ hipError_t launch_sum_nodes(const moe_cfg &c, const void *part, int part_dtype,
                             const int32_t *node_slot, void *out,
                             hipStream_t stream);
 
+// FP8 (E4M3) dispatch with per-block scales (fp8.hip).  Rows are H codes,
+// H/B fp32 scales, zero padding to a multiple of 16 bytes.
+size_t fp8_row_bytes(int H, int B);
+bool fp8_block_ok(const moe_cfg &c, int B);
+
+hipError_t launch_pack_fp8(const moe_cfg &c, int B, const void *x,
+                           const int32_t *slot_pos, void *send,
+                           hipStream_t stream);
+
+hipError_t launch_combine_fp8(const moe_cfg &c, int B, const void *y,
+                              const int32_t *slot_pos, const float *topk_w,
+                              const int32_t *topk_idx,
+                              const float *expert_scale, void *out,
+                              hipStream_t stream);
+
 }  // namespace moe

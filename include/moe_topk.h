@@ -258,6 +258,51 @@ int moe_dispatch_combine_nodes(const moe_cfg *cfg, const void *x,
                                void *out, void *ws, size_t ws_bytes,
                                hipStream_t stream);
 
+/* ---- FP8 dispatch with per-block scales ---------------------------------
+ * "Efficient and portable mixture-of-experts communication", "Envío
+ * (Dispatch)": tokens travel with block scale factors; "Workload-Static
+ * Optical Circuit Switching for Scalable LLM Inference Decode",
+ * "Communication precision": FP8 transport for MoE dispatch.  Format of a
+ * packed row (qblock B in {32, 64, 128}, H % B == 0, H % 16 == 0):
+ *   bytes [0, H)            OCP E4M3 codes (bias 7, largest magnitude 448,
+ *                           round to nearest even, sign kept)
+ *   bytes [H, H + 4H/B)     one fp32 scale per block of B elements
+ *   bytes up to the stride  zero padding; stride = moe_fp8_row_bytes(H, B),
+ *                           a multiple of 16
+ * For a block with largest magnitude amax: scale = amax / 448 and
+ * code_i = e4m3(min(max(x_i * (448 / amax), -448), 448)), each operation in
+ * fp32 with round to nearest even; a block of zeros has scale 0 and zero
+ * codes.  The dequantised value is value(code) * scale. */
+
+/* Row stride in bytes of a packed FP8 row, or 0 for an unsupported
+ * (H, qblock).  Host only. */
+size_t moe_fp8_row_bytes(int32_t H, int32_t qblock);
+
+/* Quantising pack: each token's row of x is quantised once and written to
+ * its K send rows, send + slot_pos[t*K+k] * moe_fp8_row_bytes(H, qblock).
+ * send holds T*K rows; rows no slot names are left untouched; a slot
+ * outside [0, T*K) is skipped. */
+int moe_dispatch_pack_fp8(const moe_cfg *cfg, const void *x,
+                          const int32_t *slot_pos, int32_t qblock, void *send,
+                          hipStream_t stream);
+
+/* Combine of FP8 rows: out[t] = sum_k w[t,k] * s[e(t,k)] * deq(y[slot_pos[t,k]])
+ * accumulated in fp32 and rounded once into out_dtype; other arguments as
+ * in moe_combine. */
+int moe_combine_fp8(const moe_cfg *cfg, const void *y, int32_t qblock,
+                    const int32_t *slot_pos, const float *topk_w,
+                    const int32_t *topk_idx, const float *expert_scale,
+                    void *out, hipStream_t stream);
+
+/* gate -> layout -> quantising pack -> combine of the FP8 rows through the
+ * diagonal stand-in expert.  out is computed from send, never from x. */
+int moe_dispatch_combine_fp8(const moe_cfg *cfg, const void *x,
+                             const float *logits, const float *expert_scale,
+                             int32_t *topk_idx, float *topk_w,
+                             const moe_layout *layout, int32_t qblock,
+                             void *send, void *out, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Copy the workspace error word (MOE_DEVERR_* bits, 0 when clean) to
  * *host_code after all work queued on `stream`; synchronises `stream`.  When
  * `clear` is non-zero the word is reset to 0 afterwards (enqueued). */
