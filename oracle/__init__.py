@@ -13,7 +13,9 @@ blog's "Envío (Dispatch)" and "Combinación (Combine)" sections; the two-leg
 node-level dispatch and the per-node partial combine: Cobalt Section 1 and
 "MoX: Efficient MoE Routing on Direct-Connect Topologies" Section 2.5; the
 FP8 dispatch with block scales: the blog's "Envío (Dispatch)" and the OCS
-decode paper's "Communication precision").  All are pinned by the CPU tests.
+decode paper's "Communication precision"; the capacity-padded and bucketed
+layout: the decode paper's "Variable MoE Traffic and Regularization").  All
+are pinned by the CPU tests.
 """
 from __future__ import annotations
 
@@ -71,7 +73,14 @@ def _lib() -> ctypes.CDLL:
         lib.moe_ref_pack_fp8.argtypes = [ctypes.c_int] * 5 + [_P] * 3
         lib.moe_ref_combine_fp8.argtypes = ([ctypes.c_int] * 4 + [_P] * 5 +
                                             [ctypes.c_int, _P, _P])
-        for f in ("moe_ref_pack_fp8", "moe_ref_combine_fp8"):
+        lib.moe_ref_layout_capacity.argtypes = ([ctypes.c_int] * 3 +
+                                                [_P, _P, ctypes.c_int] +
+                                                [_P] * 6)
+        lib.moe_ref_pack_capacity.argtypes = [ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_size_t, _P, _P,
+                                              ctypes.c_int, _P]
+        for f in ("moe_ref_pack_fp8", "moe_ref_combine_fp8",
+                  "moe_ref_layout_capacity", "moe_ref_pack_capacity"):
             getattr(lib, f).restype = ctypes.c_int
         for f in ("moe_ref_gate", "moe_ref_layout", "moe_ref_pack",
                   "moe_ref_combine", "moe_ref_combine_tokens",
@@ -390,6 +399,66 @@ def dispatch_combine_fp8(x: np.ndarray, logits: np.ndarray, K: int, R: int,
     send = pack_fp8(x, lay["slot_pos"], B)
     out, exact = combine_fp8(send, lay["slot_pos"], w, x.shape[1], B, idx,
                              expert_scale, out_dtype)
+    res = dict(lay)
+    res.update(topk_idx=idx, topk_w=w, send=send, out=out, out_exact=exact)
+    return res
+
+
+# ---- capacity-padded and bucketed layout ----------------------------------
+
+def capacity(T: int, K: int, E: int, gamma: float) -> int:
+    """C = ceil(gamma * T * K / E), the reading of the missing formula."""
+    return int(np.ceil(gamma * T * K / E))
+
+
+def layout_capacity(topk_idx: np.ndarray, E: int, levels) -> dict:
+    """Capacity-padded / bucketed layout (see moe_ref.c); levels ascending."""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    levels = np.ascontiguousarray(levels, dtype=np.int32)
+    T, K = topk_idx.shape
+    cmax = int(levels[-1])
+    o = {
+        "expert_count": np.empty(E, np.int32),
+        "expert_cap": np.empty(E, np.int32),
+        "expert_off": np.empty(E + 1, np.int32),
+        "slot_pos": np.empty((T, K), np.int32),
+        "row_src": np.empty(E * cmax, np.int32),
+    }
+    dropped = np.zeros(1, np.int32)
+    _check(_lib().moe_ref_layout_capacity(
+        T, E, K, _ptr(topk_idx), _ptr(levels), len(levels),
+        _ptr(o["expert_count"]), _ptr(o["expert_cap"]),
+        _ptr(o["expert_off"]), _ptr(o["slot_pos"]), _ptr(o["row_src"]),
+        _ptr(dropped)), "layout_capacity")
+    o["dropped"] = int(dropped[0])
+    return o
+
+
+def pack_capacity(x: np.ndarray, row_src: np.ndarray, K: int) -> np.ndarray:
+    """Used rows are their token's x row, padding rows are zero."""
+    x = np.ascontiguousarray(x)
+    row_src = np.ascontiguousarray(row_src, dtype=np.int32)
+    T = x.shape[0]
+    send = np.empty((len(row_src),) + x.shape[1:], dtype=x.dtype)
+    row_bytes = x[0].nbytes if T > 0 else 0
+    _check(_lib().moe_ref_pack_capacity(T, K, row_bytes, _ptr(x),
+                                        _ptr(row_src), len(row_src),
+                                        _ptr(send)), "pack_capacity")
+    return send
+
+
+def dispatch_combine_capacity(x: np.ndarray, logits: np.ndarray, K: int,
+                              levels, expert_scale: Optional[np.ndarray] = None,
+                              out_dtype: str = "bf16",
+                              renorm: bool = True) -> dict:
+    """gate -> capacity layout -> padded pack -> combine (dropped slots add
+    nothing)."""
+    idx, w = gate(logits, K, renorm)
+    E = logits.shape[1]
+    lay = layout_capacity(idx, E, levels)
+    send = pack_capacity(x, lay["row_src"], K)
+    out, exact = combine(send, lay["slot_pos"], w, idx, expert_scale,
+                         out_dtype)
     res = dict(lay)
     res.update(topk_idx=idx, topk_w=w, send=send, out=out, out_exact=exact)
     return res

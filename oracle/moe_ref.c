@@ -284,7 +284,8 @@ int moe_ref_pack(int T, int K, size_t row_bytes, const void *x,
 /* ------------------------------------------------------------------------ */
 
 /* out[t, h] = sum_k w[t,k] * s[e(t,k)] * y[slot_pos[t,k], h], summed in fp64
- * in k order; s = 1 when expert_scale is NULL (expert ids then unused).
+ * in k order; s = 1 when expert_scale is NULL (expert ids then unused).  A
+ * negative slot (a slot dropped by a capacity-limited layout) adds nothing.
  * out_exact (may be NULL) receives the unrounded fp64 sum; out (may be NULL)
  * the sum rounded to nearest-even in out_dtype. */
 int moe_ref_combine(int T, int H, int K, int y_dtype, const void *y,
@@ -298,6 +299,7 @@ int moe_ref_combine(int T, int H, int K, int y_dtype, const void *y,
       double acc = 0.0;
       for (int k = 0; k < K; ++k) {
         size_t i = (size_t)t * K + k;
+        if (slot_pos[i] < 0) continue; /* dropped slot: contributes nothing */
         double c = (double)topk_w[i];
         if (expert_scale) c *= (double)expert_scale[topk_idx[i]];
         size_t at = (size_t)slot_pos[i] * H + h;
@@ -632,6 +634,95 @@ int moe_ref_combine_fp8(int T, int H, int K, int B, const void *y,
       size_t o = (size_t)t * H + h;
       if (out_exact) out_exact[o] = acc;
       if (out) store_value(out_dtype, out, o, acc);
+    }
+  }
+  return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 7. Capacity-padded and bucketed layout                                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * "Workload-Static Optical Circuit Switching for Scalable LLM Inference
+ * Decode", section "Variable MoE Traffic and Regularization": each expert
+ * gets a fixed capacity (capacity factor gamma >= 1) and every buffer between
+ * a source group and a destination expert is padded to that many rows, so
+ * every step exchanges the same volume; tokens beyond the capacity leave on an
+ * overflow path (dropped here).  Bucketing generalises this: per-pair counts
+ * are rounded up to one of q levels C_1 < ... < C_q.  The capacity formula
+ * itself is missing from the page; the reading taken is
+ * C = ceil(gamma * T * K / E).
+ *
+ * With levels[0..q-1] ascending and Cmax = levels[q-1]:
+ *   kept_e = min(count_e, Cmax), the first kept_e tokens of expert e in
+ *            token order (the same (t, k) walk as the dropless layout);
+ *   cap_e  = the smallest level >= kept_e (q = 1: every expert gets C rows);
+ *   expert_off[E+1] = exclusive prefix of cap_e; expert e's rows are
+ *            [expert_off[e], expert_off[e] + cap_e), the first kept_e used;
+ *   slot_pos[t*K+k] = expert_off[e] + rank of t among e's tokens, or -1 when
+ *            the rank is >= Cmax (dropped);
+ *   row_src[r] = t*K+k for used rows, -1 for padding rows (E*Cmax entries);
+ *   dropped = sum_e (count_e - kept_e).
+ */
+int moe_ref_layout_capacity(int T, int E, int K, const int32_t *topk_idx,
+                            const int32_t *levels, int q,
+                            int32_t *expert_count, int32_t *expert_cap,
+                            int32_t *expert_off, int32_t *slot_pos,
+                            int32_t *row_src, int32_t *dropped) {
+  if (T < 0 || E < 1 || K < 1 || q < 1) return REF_EINVAL;
+  for (int j = 0; j < q; ++j)
+    if (levels[j] < 1 || (j > 0 && levels[j] <= levels[j - 1]))
+      return REF_EINVAL;
+  const int32_t cmax = levels[q - 1];
+  const size_t TK = (size_t)T * K;
+  for (size_t i = 0; i < TK; ++i)
+    if (topk_idx[i] < 0 || topk_idx[i] >= E) return REF_EINVAL;
+  for (int e = 0; e < E; ++e) expert_count[e] = 0;
+  for (size_t i = 0; i < TK; ++i) expert_count[topk_idx[i]] += 1;
+  int32_t drop = 0;
+  expert_off[0] = 0;
+  for (int e = 0; e < E; ++e) {
+    int32_t kept = expert_count[e] < cmax ? expert_count[e] : cmax;
+    drop += expert_count[e] - kept;
+    int32_t cap = cmax;
+    for (int j = q - 1; j >= 0; --j)
+      if (levels[j] >= kept) cap = levels[j];
+    expert_cap[e] = cap;
+    expert_off[e + 1] = expert_off[e] + cap;
+  }
+  *dropped = drop;
+  for (size_t r = 0; r < (size_t)E * cmax; ++r) row_src[r] = -1;
+  int32_t cursor[8192];
+  if (E > 8192) return REF_EINVAL;
+  for (int e = 0; e < E; ++e) cursor[e] = 0;
+  for (size_t i = 0; i < TK; ++i) {
+    int e = topk_idx[i];
+    int32_t rank = cursor[e]++;
+    if (rank < cmax) {
+      slot_pos[i] = expert_off[e] + rank;
+      row_src[slot_pos[i]] = (int32_t)i;
+    } else {
+      slot_pos[i] = -1;
+    }
+  }
+  return REF_OK;
+}
+
+/* Pack into a capacity-padded buffer of n_rows rows: a used row is the x row
+ * of its token (row_src / K), a padding row (row_src < 0) is zero. */
+int moe_ref_pack_capacity(int T, int K, size_t row_bytes, const void *x,
+                          const int32_t *row_src, int n_rows, void *send) {
+  if (T < 0 || K < 1 || n_rows < 0) return REF_EINVAL;
+  const unsigned char *src = (const unsigned char *)x;
+  unsigned char *dst = (unsigned char *)send;
+  for (int r = 0; r < n_rows; ++r) {
+    int32_t i = row_src[r];
+    if (i < 0) {
+      memset(dst + (size_t)r * row_bytes, 0, row_bytes);
+    } else {
+      if ((size_t)i >= (size_t)T * K) return REF_EINVAL;
+      memcpy(dst + (size_t)r * row_bytes, src + (size_t)(i / K) * row_bytes,
+             row_bytes);
     }
   }
   return REF_OK;
