@@ -10,14 +10,17 @@ sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload deepseek_v3] [--no-cpu-baseline]
-                       [--path flat|two_leg|fp8] [--part-dtype bf16|f32]
+                       [--path flat|two_leg|fp8|capacity] [--gamma 1.25]
+                       [--part-dtype bf16|f32]
 
 --path two_leg times moe_dispatch_combine_nodes instead: the node-level
 two-leg dispatch (one row per (token, node) crossing, then forwarded to the
 experts) and the hierarchical combine (per-node partial sums, then their sum
 at the source).  --path fp8 times moe_dispatch_combine_fp8: the pack
 quantises each row to E4M3 codes with one fp32 scale per 128 elements and the
-combine gathers and dequantises those rows.
+combine gathers and dequantises those rows.  --path capacity times
+moe_dispatch_combine_capacity with one level C = ceil(gamma*T*K/E): every
+expert's segment padded to C rows, overflow dropped.
 """
 from __future__ import annotations
 
@@ -125,7 +128,9 @@ def main() -> int:
     ap.add_argument("--fused-only", action="store_true",
                     help="time only the fused call (for profiler runs)")
     ap.add_argument("--path", default="flat",
-                    choices=("flat", "two_leg", "fp8"))
+                    choices=("flat", "two_leg", "fp8", "capacity"))
+    ap.add_argument("--gamma", type=float, default=1.25,
+                    help="capacity factor of --path capacity")
     ap.add_argument("--part-dtype", default="bf16", choices=("bf16", "f32"))
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB "
@@ -172,6 +177,9 @@ def main() -> int:
     if args.path == "two_leg":
         return two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out,
                        ws, stream)
+    if args.path == "capacity":
+        del send
+        return capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream)
     if args.path == "fp8":
         del send
         return fp8_path(args, w, cfg, x, lg, scale, idx, wt, lay, out, ws,
@@ -446,6 +454,99 @@ def fp8_path(args, w, cfg, x, lg, scale, idx, wt, lay, out, ws,
                    "seed": w.seed},
         "hbm": {"alg_bytes": alg, "gbps": gbps,
                 "frac_of_peak": gbps / HBM_PEAK_GBPS},
+        "steps_ms": steps_ms,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "alg_bytes_per_launch": kb[dom],
+                     "launch_ms": steps_ms[dom],
+                     **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
+                        for k in kb}},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream) -> int:
+    """Time moe_dispatch_combine_capacity (one capacity level); JSON line."""
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    C = int(np.ceil(args.gamma * w.T * w.K / w.E))
+    levels = [C]
+    n_rows = w.E * C
+    lay = moe.alloc_capacity_layout(cfg, levels, x.device)
+    ws = moe.alloc_capacity_workspace(cfg, x.device)
+    send = torch.empty((n_rows, w.H), dtype=x.dtype, device=x.device)
+
+    def step():
+        moe.moe_dispatch_combine_capacity(cfg, x, lg, scale, idx, wt, levels,
+                                          lay, send, out, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dropped = int(lay.dropped[0].item())
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"bench: capacity {ms:.4f} ms/step, C={C}, dropped {dropped}",
+          file=sys.stderr, flush=True)
+
+    b, ob = w.elem_bytes, w.out_elem_bytes
+    T, H, K = w.T, w.H, w.K
+    kept = T * K - dropped
+    kb = {"pack_capacity": T * H * b + n_rows * H * b + 4 * T * K + 4 * n_rows,
+          "combine_capacity": kept * H * b + T * H * ob + 12 * T * K}
+    meta = T * (4 * w.E + 32 * K + 8) + 8 * w.E
+    alg = kb["pack_capacity"] + kb["combine_capacity"] + meta
+    n = max(args.steps, 5)
+    names = ("gate", "layout_capacity", "pack_capacity", "combine_capacity")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+           for _ in range(n)]
+    for i in range(n):
+        e = evs[i]
+        e[0].record(stream)
+        moe.moe_topk_gate(cfg, lg, idx, wt, stream)
+        e[1].record(stream)
+        moe.moe_dispatch_layout_capacity(cfg, idx, levels, lay, ws, stream)
+        e[2].record(stream)
+        moe.moe_dispatch_pack_capacity(cfg, x, lay.slot_pos, lay.row_src,
+                                       send, stream)
+        e[3].record(stream)
+        moe.moe_combine_capacity(cfg, send, lay.slot_pos, wt, idx, scale, out,
+                                 stream)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    steps_ms = {nm: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                   for i in range(n)]))
+                for j, nm in enumerate(names)}
+    dom = max(kb, key=lambda k: steps_ms[k])
+    achieved = kb[dom] / (steps_ms[dom] * 1e-3) / 1e9
+    gbps = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.x_dtype == mi.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "path": "capacity", "T": T, "H": H,
+                   "E": w.E, "K": K, "R": w.R, "N": w.N, "gamma": args.gamma,
+                   "capacity": C, "rows": w.x_dtype, "accumulate": "f32",
+                   "seed": w.seed},
+        "hbm": {"alg_bytes": alg, "gbps": gbps,
+                "frac_of_peak": gbps / HBM_PEAK_GBPS},
+        "capacity": {"rows": n_rows, "slots": T * K, "dropped": dropped,
+                     "pad_ratio": n_rows / (T * K),
+                     "drop_rate": dropped / (T * K)},
         "steps_ms": steps_ms,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

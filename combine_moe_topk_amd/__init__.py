@@ -8,7 +8,9 @@ and the node-level two-leg path :func:`moe_dispatch_pack_nodes`,
 :func:`moe_dispatch_forward`, :func:`moe_combine_partial`,
 :func:`moe_combine_nodes`, :func:`moe_dispatch_combine_nodes`, and the FP8
 dispatch :func:`moe_dispatch_pack_fp8`, :func:`moe_combine_fp8`,
-:func:`moe_dispatch_combine_fp8`.
+:func:`moe_dispatch_combine_fp8`, and the capacity-padded / bucketed layout
+:func:`moe_dispatch_layout_capacity`, :func:`moe_dispatch_pack_capacity`,
+:func:`moe_combine_capacity`, :func:`moe_dispatch_combine_capacity`.
 """
 from ._lib import (  # noqa: F401
     LAYOUT_FIELDS, Layout, MoeError, MOE_BF16, MOE_DEVERR_DUP_EXPERT,
@@ -22,4 +24,8 @@ from ._lib import (  # noqa: F401
     moe_combine_partial, moe_combine_nodes, moe_dispatch_combine_nodes,
     moe_fp8_row_bytes, moe_dispatch_pack_fp8, moe_combine_fp8,
     moe_dispatch_combine_fp8,
+    MOE_MAX_LEVELS, CapacityLayout, moe_capacity_layout,
+    alloc_capacity_layout, alloc_capacity_workspace,
+    moe_dispatch_layout_capacity, moe_dispatch_pack_capacity,
+    moe_combine_capacity, moe_dispatch_combine_capacity,
 )

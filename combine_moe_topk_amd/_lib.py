@@ -56,10 +56,23 @@ class moe_layout(ctypes.Structure):
 
 LAYOUT_FIELDS = [n for n, _ in moe_layout._fields_]
 
+MOE_MAX_LEVELS = 8
+
+
+class moe_capacity_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "expert_count", "expert_cap", "expert_off", "slot_pos", "row_src",
+        "dropped")]
+
+
+CAP_FIELDS = [n for n, _ in moe_capacity_layout._fields_]
+
 _LIB: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _CFG = ctypes.POINTER(moe_cfg)
 _LAY = ctypes.POINTER(moe_layout)
+_CAP = ctypes.POINTER(moe_capacity_layout)
+_I32P = ctypes.POINTER(ctypes.c_int32)
 
 
 def lib() -> ctypes.CDLL:
@@ -105,6 +118,17 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_combine_fp8": (ctypes.c_int, [
                 _CFG, _P, _P, _P, _P, _P, _LAY, ctypes.c_int32, _P, _P, _P,
                 ctypes.c_size_t, _P]),
+            "moe_capacity_workspace_bytes": (ctypes.c_size_t, [_CFG]),
+            "moe_dispatch_layout_capacity": (ctypes.c_int, [
+                _CFG, _P, _I32P, ctypes.c_int32, _CAP, _P, ctypes.c_size_t,
+                _P]),
+            "moe_dispatch_pack_capacity": (ctypes.c_int, [
+                _CFG, _P, _P, _P, ctypes.c_int32, _P, _P]),
+            "moe_combine_capacity": (ctypes.c_int, [
+                _CFG, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+            "moe_dispatch_combine_capacity": (ctypes.c_int, [
+                _CFG, _P, _P, _P, _P, _P, _I32P, ctypes.c_int32, _CAP, _P, _P,
+                _P, ctypes.c_size_t, _P]),
             "moe_read_device_error": (ctypes.c_int, [_P, _P,
                                                      ctypes.POINTER(ctypes.c_int32),
                                                      ctypes.c_int]),
@@ -424,6 +448,110 @@ def moe_dispatch_combine_fp8(cfg: moe_cfg, x: torch.Tensor,
         _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
         "moe_dispatch_combine_fp8")
+
+
+# ---- capacity-padded and bucketed layout ----------------------------------
+
+@dataclasses.dataclass
+class CapacityLayout:
+    """Device tensors receiving the capacity layout (``moe_capacity_layout``)."""
+
+    expert_count: torch.Tensor
+    expert_cap: torch.Tensor
+    expert_off: torch.Tensor
+    slot_pos: torch.Tensor
+    row_src: torch.Tensor
+    dropped: torch.Tensor
+
+    def c_struct(self) -> moe_capacity_layout:
+        return moe_capacity_layout(*[_ptr(getattr(self, n), torch.int32, n)
+                                     for n in CAP_FIELDS])
+
+
+def alloc_capacity_layout(cfg: moe_cfg, levels, device="cuda") -> CapacityLayout:
+    def i32(n):
+        return torch.empty(max(n, 0), dtype=torch.int32, device=device)
+    cmax = int(levels[-1])
+    return CapacityLayout(expert_count=i32(cfg.E), expert_cap=i32(cfg.E),
+                          expert_off=i32(cfg.E + 1),
+                          slot_pos=i32(cfg.T * cfg.K),
+                          row_src=i32(cfg.E * cmax), dropped=i32(1))
+
+
+def alloc_capacity_workspace(cfg: moe_cfg, device="cuda",
+                             stream=None) -> torch.Tensor:
+    n = lib().moe_capacity_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise MoeError(moe_validate_cfg(cfg), "moe_capacity_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_workspace_init(ws, stream)
+    return ws
+
+
+def _levels(levels):
+    arr = (ctypes.c_int32 * len(levels))(*[int(v) for v in levels])
+    return arr, len(levels)
+
+
+def moe_dispatch_layout_capacity(cfg: moe_cfg, topk_idx: torch.Tensor, levels,
+                                 layout: CapacityLayout, ws: torch.Tensor,
+                                 stream=None) -> None:
+    lv, q = _levels(levels)
+    lay = layout.c_struct()
+    _check(lib().moe_dispatch_layout_capacity(
+        ctypes.byref(cfg), _ptr(topk_idx, torch.int32, "topk_idx"), lv, q,
+        ctypes.byref(lay), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+        _stream(stream)), "moe_dispatch_layout_capacity")
+
+
+def moe_dispatch_pack_capacity(cfg: moe_cfg, x: torch.Tensor,
+                               slot_pos: torch.Tensor, row_src: torch.Tensor,
+                               send: torch.Tensor, stream=None) -> None:
+    if row_src.numel() < send.shape[0]:
+        raise ValueError("row_src must have one entry per send row")
+    _check(lib().moe_dispatch_pack_capacity(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(slot_pos, torch.int32, "slot_pos"),
+        _ptr(row_src, torch.int32, "row_src"), send.shape[0],
+        _ptr(send, _row_dtype(cfg), "send"), _stream(stream)),
+        "moe_dispatch_pack_capacity")
+
+
+def moe_combine_capacity(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
+                         topk_w: torch.Tensor, topk_idx: Optional[torch.Tensor],
+                         expert_scale: Optional[torch.Tensor],
+                         out: torch.Tensor, stream=None) -> None:
+    _check(lib().moe_combine_capacity(
+        ctypes.byref(cfg), _ptr(y, _row_dtype(cfg), "y"), y.shape[0],
+        _ptr(slot_pos, torch.int32, "slot_pos"),
+        _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"), _stream(stream)),
+        "moe_combine_capacity")
+
+
+def moe_dispatch_combine_capacity(cfg: moe_cfg, x: torch.Tensor,
+                                  logits: torch.Tensor,
+                                  expert_scale: Optional[torch.Tensor],
+                                  topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                                  levels, layout: CapacityLayout,
+                                  send: torch.Tensor, out: torch.Tensor,
+                                  ws: torch.Tensor, stream=None) -> None:
+    lv, q = _levels(levels)
+    if send.shape[0] != cfg.E * int(levels[-1]):
+        raise ValueError("send must have E * levels[-1] rows")
+    lay = layout.c_struct()
+    _check(lib().moe_dispatch_combine_capacity(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"), lv, q, ctypes.byref(lay),
+        _ptr(send, _row_dtype(cfg), "send"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+        "moe_dispatch_combine_capacity")
 
 
 def moe_read_device_error(ws: torch.Tensor, clear: bool = True,

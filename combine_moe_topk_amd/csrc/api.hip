@@ -326,6 +326,101 @@ int moe_dispatch_combine_fp8(const moe_cfg *cfg, const void *x,
   return launch_status(e);
 }
 
+size_t moe_capacity_workspace_bytes(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  return moe::capacity_ws_bytes(*cfg);
+}
+
+static int check_cap_layout(const moe_cfg *c, const moe_capacity_layout *l) {
+  if (!l || !l->expert_count || !l->expert_cap || !l->expert_off ||
+      !l->row_src || !l->dropped)
+    return MOE_EINVAL;
+  if (c->T > 0 && !l->slot_pos) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int moe_dispatch_layout_capacity(const moe_cfg *cfg, const int32_t *topk_idx,
+                                 const int32_t *levels, int32_t q,
+                                 const moe_capacity_layout *layout, void *ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!moe::levels_ok(*cfg, levels, q)) return MOE_EINVAL;
+  if ((rc = check_cap_layout(cfg, layout)) != MOE_OK) return rc;
+  if (cfg->T > 0 && !topk_idx) return MOE_EINVAL;
+  if (!ws) return MOE_EWORKSPACE;
+  if (!aligned(ws, 256)) return MOE_EUNSUPPORTED;
+  if (ws_bytes < moe::capacity_ws_bytes(*cfg)) return MOE_EWORKSPACE;
+  return launch_status(moe::launch_layout_capacity(*cfg, topk_idx, levels, q,
+                                                   *layout, ws, stream));
+}
+
+int moe_dispatch_pack_capacity(const moe_cfg *cfg, const void *x,
+                               const int32_t *slot_pos,
+                               const int32_t *row_src, int32_t n_rows,
+                               void *send, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (n_rows < 0) return MOE_EINVAL;
+  if (n_rows == 0 && cfg->T == 0) return MOE_OK;
+  if (!send || !row_src || (cfg->T > 0 && (!x || !slot_pos)))
+    return MOE_EINVAL;
+  if ((x && !aligned16(x)) || !aligned16(send)) return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_pack_capacity(*cfg, x, slot_pos, row_src,
+                                                 n_rows, send, stream));
+}
+
+int moe_combine_capacity(const moe_cfg *cfg, const void *y, int32_t n_rows,
+                         const int32_t *slot_pos, const float *topk_w,
+                         const int32_t *topk_idx, const float *expert_scale,
+                         void *out, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (n_rows < 0) return MOE_EINVAL;
+  if (cfg->T == 0) return MOE_OK;
+  if (!y || !slot_pos || !topk_w || !out) return MOE_EINVAL;
+  if (expert_scale && !topk_idx) return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(out)) return MOE_EUNSUPPORTED;
+  return launch_status(moe::launch_combine(*cfg, y, slot_pos, topk_w,
+                                           topk_idx, expert_scale, out,
+                                           stream, n_rows));
+}
+
+int moe_dispatch_combine_capacity(const moe_cfg *cfg, const void *x,
+                                  const float *logits,
+                                  const float *expert_scale,
+                                  int32_t *topk_idx, float *topk_w,
+                                  const int32_t *levels, int32_t q,
+                                  const moe_capacity_layout *layout,
+                                  void *send, void *out, void *ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!moe::levels_ok(*cfg, levels, q)) return MOE_EINVAL;
+  if ((rc = check_cap_layout(cfg, layout)) != MOE_OK) return rc;
+  if (!ws) return MOE_EWORKSPACE;
+  if (!aligned(ws, 256)) return MOE_EUNSUPPORTED;
+  if (ws_bytes < moe::capacity_ws_bytes(*cfg)) return MOE_EWORKSPACE;
+  if (!send) return MOE_EINVAL;
+  if (cfg->T > 0) {
+    if (!x || !logits || !topk_idx || !topk_w || !out) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(out)) return MOE_EUNSUPPORTED;
+  }
+  if (!aligned16(send)) return MOE_EUNSUPPORTED;
+  const int n_rows = cfg->E * levels[q - 1];
+  hipError_t e = moe::launch_gate(*cfg, logits, topk_idx, topk_w, stream);
+  if (e == hipSuccess)
+    e = moe::launch_layout_capacity(*cfg, topk_idx, levels, q, *layout, ws,
+                                    stream);
+  if (e == hipSuccess)
+    e = moe::launch_pack_capacity(*cfg, x, layout->slot_pos, layout->row_src,
+                                  n_rows, send, stream);
+  if (e == hipSuccess)
+    e = moe::launch_combine(*cfg, send, layout->slot_pos, topk_w, topk_idx,
+                            expert_scale, out, stream, n_rows);
+  return launch_status(e);
+}
+
 int moe_read_device_error(const void *ws, hipStream_t stream,
                           int32_t *host_code, int clear) {
   if (!ws || !host_code) return MOE_EINVAL;

@@ -126,38 +126,38 @@ constexpr int upt_for() {
 template <bool YB, bool OB, int KT, int TPT>
 hipError_t launch_kt(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                      const float *w, const int32_t *idx, const float *scale,
-                     void *out, hipStream_t s) {
+                     void *out, int rows, hipStream_t s) {
   constexpr int UPT = upt_for<YB, KT>();
   constexpr int kTokensPerBlock = 256 / TPT;
   const int U = c.H / 8;
   const int grid = (c.T + kTokensPerBlock - 1) / kTokensPerBlock;
   hipLaunchKernelGGL((combine_kernel<YB, OB, KT, UPT, TPT>), dim3(grid),
                      dim3(256), 0, s, (const char *)y, slot_pos, w, idx,
-                     scale, (char *)out, c.T, c.K, U, c.T * c.K);
+                     scale, (char *)out, c.T, c.K, U, rows);
   return hipGetLastError();
 }
 
 template <bool YB, bool OB, int KT>
 hipError_t launch_k(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                     const float *w, const int32_t *idx, const float *scale,
-                    void *out, hipStream_t s) {
+                    void *out, int rows, hipStream_t s) {
   // one wave per token while 64*UPT units cover the row, else a workgroup
   if (c.H / 8 <= 64 * upt_for<YB, KT>())
-    return launch_kt<YB, OB, KT, 64>(c, y, slot_pos, w, idx, scale, out, s);
-  return launch_kt<YB, OB, KT, 256>(c, y, slot_pos, w, idx, scale, out, s);
+    return launch_kt<YB, OB, KT, 64>(c, y, slot_pos, w, idx, scale, out, rows, s);
+  return launch_kt<YB, OB, KT, 256>(c, y, slot_pos, w, idx, scale, out, rows, s);
 }
 
 template <bool YB, bool OB>
 hipError_t launch_d(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                     const float *w, const int32_t *idx, const float *scale,
-                    void *out, hipStream_t s) {
+                    void *out, int rows, hipStream_t s) {
   switch (c.K) {
-    case 1: return launch_k<YB, OB, 1>(c, y, slot_pos, w, idx, scale, out, s);
-    case 2: return launch_k<YB, OB, 2>(c, y, slot_pos, w, idx, scale, out, s);
-    case 4: return launch_k<YB, OB, 4>(c, y, slot_pos, w, idx, scale, out, s);
-    case 8: return launch_k<YB, OB, 8>(c, y, slot_pos, w, idx, scale, out, s);
-    case 16: return launch_k<YB, OB, 16>(c, y, slot_pos, w, idx, scale, out, s);
-    default: return launch_k<YB, OB, 0>(c, y, slot_pos, w, idx, scale, out, s);
+    case 1: return launch_k<YB, OB, 1>(c, y, slot_pos, w, idx, scale, out, rows, s);
+    case 2: return launch_k<YB, OB, 2>(c, y, slot_pos, w, idx, scale, out, rows, s);
+    case 4: return launch_k<YB, OB, 4>(c, y, slot_pos, w, idx, scale, out, rows, s);
+    case 8: return launch_k<YB, OB, 8>(c, y, slot_pos, w, idx, scale, out, rows, s);
+    case 16: return launch_k<YB, OB, 16>(c, y, slot_pos, w, idx, scale, out, rows, s);
+    default: return launch_k<YB, OB, 0>(c, y, slot_pos, w, idx, scale, out, rows, s);
   }
 }
 
@@ -166,17 +166,18 @@ hipError_t launch_d(const moe_cfg &c, const void *y, const int32_t *slot_pos,
 hipError_t launch_combine(const moe_cfg &c, const void *y,
                           const int32_t *slot_pos, const float *topk_w,
                           const int32_t *topk_idx, const float *expert_scale,
-                          void *out, hipStream_t stream) {
+                          void *out, hipStream_t stream, int rows) {
   if (c.T == 0) return hipSuccess;
+  if (rows < 0) rows = c.T * c.K;
   const bool yb = c.x_dtype == MOE_BF16;
   const bool ob = c.out_dtype == MOE_BF16;
   if (yb && ob)
-    return launch_d<true, true>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
+    return launch_d<true, true>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, rows, stream);
   if (yb && !ob)
-    return launch_d<true, false>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
+    return launch_d<true, false>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, rows, stream);
   if (!yb && ob)
-    return launch_d<false, true>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
-  return launch_d<false, false>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, stream);
+    return launch_d<false, true>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, rows, stream);
+  return launch_d<false, false>(c, y, slot_pos, topk_w, topk_idx, expert_scale, out, rows, stream);
 }
 
 }  // namespace moe

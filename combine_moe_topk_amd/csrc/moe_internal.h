@@ -14,6 +14,7 @@ constexpr int kWave = 64;            // CDNA wavefront width
 constexpr size_t kWsHeader = 256;    // workspace header: error word + pad
 constexpr int kLdsBudget = 65536;    // bytes of LDS a layout workgroup may use
 constexpr int kDefaultLayoutTile = 256;
+constexpr int kMaxLevels = MOE_MAX_LEVELS;  // capacity / bucket levels
 
 // 16-byte vector used for every row copy (one global_load/store_dwordx4).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -51,10 +52,11 @@ hipError_t launch_pack(const moe_cfg &c, const void *x,
                        const int32_t *slot_pos, void *send,
                        hipStream_t stream);
 
+// rows: rows of y (slots outside [0, rows) add 0); -1 means T*K.
 hipError_t launch_combine(const moe_cfg &c, const void *y,
                           const int32_t *slot_pos, const float *topk_w,
                           const int32_t *topk_idx, const float *expert_scale,
-                          void *out, hipStream_t stream);
+                          void *out, hipStream_t stream, int rows = -1);
 
 // Node-level two-leg dispatch and hierarchical combine (nodes.hip).  Leg-1
 // and partial buffers hold node_rows_max(c) = T * min(K, N) rows.
@@ -93,5 +95,19 @@ hipError_t launch_combine_fp8(const moe_cfg &c, int B, const void *y,
                               const int32_t *topk_idx,
                               const float *expert_scale, void *out,
                               hipStream_t stream);
+
+// Capacity-padded and bucketed layout (capacity.hip).
+bool levels_ok(const moe_cfg &c, const int32_t *levels, int q);
+size_t capacity_ws_bytes(const moe_cfg &c);
+
+hipError_t launch_layout_capacity(const moe_cfg &c, const int32_t *topk_idx,
+                                  const int32_t *levels, int q,
+                                  const moe_capacity_layout &cl, void *ws,
+                                  hipStream_t stream);
+
+hipError_t launch_pack_capacity(const moe_cfg &c, const void *x,
+                                const int32_t *slot_pos,
+                                const int32_t *row_src, int n_rows,
+                                void *send, hipStream_t stream);
 
 }  // namespace moe

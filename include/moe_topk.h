@@ -303,6 +303,72 @@ int moe_dispatch_combine_fp8(const moe_cfg *cfg, const void *x,
                              void *send, void *out, void *ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* ---- capacity-padded and bucketed layout -------------------------------
+ * "Workload-Static Optical Circuit Switching for Scalable LLM Inference
+ * Decode", "Variable MoE Traffic and Regularization": every buffer between a
+ * source and a destination expert is padded to a fixed capacity, so each
+ * step moves the same volume, and rows beyond it are dropped; bucketing
+ * rounds each count up to one of q levels C_1 < ... < C_q.  The page's
+ * capacity formula is missing; C = ceil(gamma * T * K / E) is the intended
+ * use (levels = {C}).  With Cmax = levels[q-1]:
+ *   kept_e  = min(expert_count[e], Cmax): expert e keeps its first kept_e
+ *             tokens in token order, the rest are dropped;
+ *   expert_cap[e] = smallest level >= kept_e; expert_off = exclusive prefix;
+ *   slot_pos[t*K+k] = expert_off[e] + rank of t among e's tokens, or -1;
+ *   row_src[r] = t*K + k for used rows, -1 for padding rows
+ *                (E * Cmax entries, the capacity of a send buffer);
+ *   *dropped = sum_e (expert_count[e] - kept_e).
+ * A dropped (t, k) adds nothing in the combine; the other weights are not
+ * rescaled. */
+#define MOE_MAX_LEVELS 8
+
+typedef struct moe_capacity_layout {
+  int32_t *expert_count; /* [E]   times expert e was chosen               */
+  int32_t *expert_cap;   /* [E]   rows of expert e's padded segment       */
+  int32_t *expert_off;   /* [E+1] first row of each segment              */
+  int32_t *slot_pos;     /* [T*K] send row of (t,k), -1 when dropped      */
+  int32_t *row_src;      /* [E*Cmax] t*K+k of a used row, -1 for padding  */
+  int32_t *dropped;      /* [1]   number of dropped (t,k)                 */
+} moe_capacity_layout;
+
+/* Workspace bytes moe_dispatch_layout_capacity and
+ * moe_dispatch_combine_capacity need (0 when cfg is invalid).  Host only. */
+size_t moe_capacity_workspace_bytes(const moe_cfg *cfg);
+
+/* Capacity-padded / bucketed layout of topk_idx.  levels is a HOST array of
+ * q (1..MOE_MAX_LEVELS) strictly increasing positive row counts; every
+ * output pointer of `layout` is required. */
+int moe_dispatch_layout_capacity(const moe_cfg *cfg, const int32_t *topk_idx,
+                                 const int32_t *levels, int32_t q,
+                                 const moe_capacity_layout *layout, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Pack into a padded send buffer of n_rows rows: used rows receive their
+ * token's x row, rows with row_src < 0 are set to zero.  row_src must hold
+ * n_rows entries (n_rows <= E * Cmax for the layout's row_src). */
+int moe_dispatch_pack_capacity(const moe_cfg *cfg, const void *x,
+                               const int32_t *slot_pos,
+                               const int32_t *row_src, int32_t n_rows,
+                               void *send, hipStream_t stream);
+
+/* moe_combine over a padded buffer y of n_rows rows; slots outside
+ * [0, n_rows) (dropped ones are -1) add nothing. */
+int moe_combine_capacity(const moe_cfg *cfg, const void *y, int32_t n_rows,
+                         const int32_t *slot_pos, const float *topk_w,
+                         const int32_t *topk_idx, const float *expert_scale,
+                         void *out, hipStream_t stream);
+
+/* gate -> capacity layout -> padded pack -> combine through the stand-in
+ * expert; send has E * levels[q-1] rows.  out is computed from send. */
+int moe_dispatch_combine_capacity(const moe_cfg *cfg, const void *x,
+                                  const float *logits,
+                                  const float *expert_scale,
+                                  int32_t *topk_idx, float *topk_w,
+                                  const int32_t *levels, int32_t q,
+                                  const moe_capacity_layout *layout,
+                                  void *send, void *out, void *ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /* Copy the workspace error word (MOE_DEVERR_* bits, 0 when clean) to
  * *host_code after all work queued on `stream`; synchronises `stream`.  When
  * `clear` is non-zero the word is reset to 0 afterwards (enqueued). */

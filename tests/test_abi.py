@@ -151,3 +151,30 @@ def test_node_entry_points_declared_and_validated():
     assert lib.moe_dispatch_combine_nodes(
         ctypes.byref(c), None, None, None, None, None, ctypes.byref(lay),
         None, None, moe.MOE_BF16, None, None, None, 0, None) == moe.MOE_EINVAL
+
+
+def test_capacity_entry_points_validate_on_host():
+    names = declared_functions()
+    for n in ("moe_capacity_workspace_bytes", "moe_dispatch_layout_capacity",
+              "moe_dispatch_pack_capacity", "moe_combine_capacity",
+              "moe_dispatch_combine_capacity", "moe_fp8_row_bytes",
+              "moe_dispatch_pack_fp8", "moe_combine_fp8",
+              "moe_dispatch_combine_fp8"):
+        assert n in names
+    assert ctypes.sizeof(moe.moe_capacity_layout) == 6 * 8
+    c = cfg()
+    ws = moe.lib().moe_capacity_workspace_bytes(ctypes.byref(c))
+    assert ws > moe.moe_workspace_bytes(c) + 16384 * 8 * 4
+    lib = moe.lib()
+    lay = moe.moe_capacity_layout()
+    lv = (ctypes.c_int32 * 3)(64, 32, 128)           # not increasing
+    assert lib.moe_dispatch_layout_capacity(ctypes.byref(c), None, lv, 3,
+                                            ctypes.byref(lay), None, 0,
+                                            None) == moe.MOE_EINVAL
+    lv = (ctypes.c_int32 * 9)(*range(1, 10))          # too many levels
+    assert lib.moe_dispatch_layout_capacity(ctypes.byref(c), None, lv, 9,
+                                            ctypes.byref(lay), None, 0,
+                                            None) == moe.MOE_EINVAL
+    assert moe.moe_fp8_row_bytes(7168, 128) == 7168 + 224
+    assert moe.moe_fp8_row_bytes(256, 128) == 272
+    assert moe.moe_fp8_row_bytes(100, 32) == 0
