@@ -232,6 +232,44 @@ def random_topk_idx(T: int, E: int, K: int, seed: int = 0) -> np.ndarray:
     return np.argsort(keys, axis=1)[:, :K].astype(np.int32)
 
 
+def replica_layout(E: int, G: int, rho: float, seed: int = 0) -> np.ndarray:
+    """A seeded expert layout with replicas: holds[r, e] = 1 when rank r has a
+    replica of expert e (uint8 [G, E]).
+
+    Every expert keeps its contiguous home rank e // (E/G); then round(rho*E)
+    extra replicas go, one at a time, to a uniformly drawn expert and a
+    uniformly drawn rank that does not hold it yet and has a free slot, with
+    at most ceil((1 + rho) * E / G) replicas per rank (the replica budget of
+    "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+    Training", Section 3.1).  Stands in for the planner's layout, which is
+    not built.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    holds = np.zeros((G, E), np.uint8)
+    holds[np.arange(E) // (E // G), np.arange(E)] = 1
+    budget = int(np.ceil((1.0 + rho) * E / G))
+    extra = int(round(rho * E))
+    placed = 0
+    tries = 0
+    while placed < extra and tries < 100 * max(extra, 1):
+        tries += 1
+        e = int(rng.integers(0, E))
+        free = np.nonzero((holds[:, e] == 0) & (holds.sum(axis=1) < budget))[0]
+        if len(free) == 0:
+            continue
+        holds[int(rng.choice(free)), e] = 1
+        placed += 1
+    return holds
+
+
+def assign_draws(T: int, K: int, seed: int = 0):
+    """Uniform uint32 draws for the task assignment's random choices:
+    (u_node, u_rank), each uint32 [T, K]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = rng.integers(0, 1 << 32, size=(2, T, K), dtype=np.uint64)
+    return u[0].astype(np.uint32), u[1].astype(np.uint32)
+
+
 def ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
@@ -242,4 +280,5 @@ __all__ = [
     "expert_scale", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "logits_all_equal", "logits_signed_zeros", "logits_few_levels",
     "logits_one_hot_experts", "random_x", "random_topk_idx", "ceil_div",
+    "replica_layout", "assign_draws",
 ]

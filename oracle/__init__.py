@@ -14,8 +14,8 @@ node-level dispatch and the per-node partial combine: Cobalt Section 1 and
 "MoX: Efficient MoE Routing on Direct-Connect Topologies" Section 2.5; the
 FP8 dispatch with block scales: the blog's "Envío (Dispatch)" and the OCS
 decode paper's "Communication precision"; the capacity-padded and bucketed
-layout: the decode paper's "Variable MoE Traffic and Regularization").  All
-are pinned by the CPU tests.
+layout: the decode paper's "Variable MoE Traffic and Regularization"; the task
+assignment: Cobalt Section 3.3).  All are pinned by the CPU tests.
 """
 from __future__ import annotations
 
@@ -79,6 +79,8 @@ def _lib() -> ctypes.CDLL:
         lib.moe_ref_pack_capacity.argtypes = [ctypes.c_int, ctypes.c_int,
                                               ctypes.c_size_t, _P, _P,
                                               ctypes.c_int, _P]
+        lib.moe_ref_assign.argtypes = [ctypes.c_int] * 5 + [_P] * 7
+        lib.moe_ref_assign.restype = ctypes.c_int
         for f in ("moe_ref_pack_fp8", "moe_ref_combine_fp8",
                   "moe_ref_layout_capacity", "moe_ref_pack_capacity"):
             getattr(lib, f).restype = ctypes.c_int
@@ -462,6 +464,29 @@ def dispatch_combine_capacity(x: np.ndarray, logits: np.ndarray, K: int,
     res = dict(lay)
     res.update(topk_idx=idx, topk_w=w, send=send, out=out, out_exact=exact)
     return res
+
+
+# ---- communication-aware task assignment -----------------------------------
+
+def assign(topk_idx: np.ndarray, src_rank: np.ndarray, holds: np.ndarray,
+           N: int, u_node: np.ndarray, u_rank: np.ndarray):
+    """Cobalt Section 3.3 task assignment (see moe_ref.c).
+
+    Returns ``(assign_rank int32 [T,K], remote_mask uint64 [T])``.
+    """
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    src_rank = np.ascontiguousarray(src_rank, dtype=np.int32)
+    holds = np.ascontiguousarray(holds, dtype=np.uint8)
+    u_node = np.ascontiguousarray(u_node, dtype=np.uint32)
+    u_rank = np.ascontiguousarray(u_rank, dtype=np.uint32)
+    T, K = topk_idx.shape
+    G, E = holds.shape
+    ar = np.empty((T, K), np.int32)
+    rm = np.empty(T, np.uint64)
+    _check(_lib().moe_ref_assign(T, E, K, G, N, _ptr(topk_idx),
+                                 _ptr(src_rank), _ptr(holds), _ptr(u_node),
+                                 _ptr(u_rank), _ptr(ar), _ptr(rm)), "assign")
+    return ar, rm
 
 
 def f64_to_bf16(values) -> np.ndarray:

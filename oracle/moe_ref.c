@@ -727,3 +727,112 @@ int moe_ref_pack_capacity(int T, int K, size_t row_bytes, const void *x,
   }
   return REF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 8. Communication-aware task assignment                                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+ * Training", Section 3.3 (Algorithm 1).  G ranks on N nodes, G/N contiguous
+ * ranks per node; holds[r*E + e] != 0 when rank r has a replica of expert e.
+ * For token t with source rank src_rank[t] on node sn:
+ *   Step 1: a selected expert with a replica on node sn runs on node sn; the
+ *   others (the set U) need remote nodes.  For e in U, m_e = the remote
+ *   nodes holding e.  A mask b of remote nodes is feasible when b & m_e != 0
+ *   for every e in U; the chosen b is a feasible mask of smallest popcount
+ *   (the minimum set cover), and among those the one of smallest value (the
+ *   page does not say which; masks are enumerated by popcount, then value).
+ *   Each e in U runs on a node drawn from b & m_e.
+ *   Step 2: the rank is drawn from the ranks of that node holding e.
+ * Random draws are inputs: a draw u (uint32) picks entry floor(u * c / 2^32)
+ * of a list of c candidates in ascending order.
+ * Outputs: assign_rank[t*K+k], remote_mask[t] = b.  Returns REF_EINVAL when
+ * an expert has no replica at all or a shape is bad.
+ */
+static int pick(uint32_t u, int c) {
+  return (int)(((uint64_t)u * (uint64_t)c) >> 32);
+}
+
+int moe_ref_assign(int T, int E, int K, int G, int N, const int32_t *topk_idx,
+                   const int32_t *src_rank, const uint8_t *holds,
+                   const uint32_t *u_node, const uint32_t *u_rank,
+                   int32_t *assign_rank, uint64_t *remote_mask) {
+  /* the oracle scans all 2^N masks: small N only */
+  if (T < 0 || E < 1 || K < 1 || G < 1 || N < 1 || N > 24 || G % N != 0)
+    return REF_EINVAL;
+  const int per_node = G / N;
+  for (int t = 0; t < T; ++t) {
+    const int sr = src_rank[t];
+    if (sr < 0 || sr >= G) return REF_EINVAL;
+    const int sn = sr / per_node;
+    uint64_t m[64];   /* remote nodes holding each selected expert */
+    int in_u[64];
+    if (K > 64) return REF_EINVAL;
+    int n_u = 0;
+    for (int k = 0; k < K; ++k) {
+      const int e = topk_idx[(size_t)t * K + k];
+      if (e < 0 || e >= E) return REF_EINVAL;
+      uint64_t nodes = 0;
+      for (int r = 0; r < G; ++r)
+        if (holds[(size_t)r * E + e]) nodes |= (uint64_t)1 << (r / per_node);
+      if (nodes == 0) return REF_EINVAL;
+      in_u[k] = !((nodes >> sn) & 1);
+      m[k] = nodes & ~((uint64_t)1 << sn);
+      n_u += in_u[k];
+    }
+    /* Step 1: smallest-popcount feasible mask, then smallest value: scan
+     * every mask of popcount p (bit sn clear) in increasing value */
+    uint64_t best = 0;
+    if (n_u > 0) {
+      int found = 0;
+      for (int p = 1; p <= N - 1 && !found; ++p) {
+        for (uint64_t b = 1; b < ((uint64_t)1 << N); ++b) {
+          if (__builtin_popcountll(b) != p || ((b >> sn) & 1)) continue;
+          int ok = 1;
+          for (int k = 0; k < K && ok; ++k)
+            if (in_u[k] && !(b & m[k])) ok = 0;
+          if (ok) {
+            best = b;
+            found = 1;
+            break;
+          }
+        }
+      }
+      if (!found) return REF_EINVAL;
+    }
+    remote_mask[t] = best;
+    for (int k = 0; k < K; ++k) {
+      const size_t i = (size_t)t * K + k;
+      const int e = topk_idx[i];
+      int node = sn;
+      if (in_u[k]) {
+        uint64_t cand = best & m[k];
+        int j = pick(u_node[i], __builtin_popcountll(cand));
+        for (int n = 0; n < N; ++n)
+          if ((cand >> n) & 1) {
+            if (j == 0) {
+              node = n;
+              break;
+            }
+            --j;
+          }
+      }
+      /* Step 2: uniform among node's ranks holding e, ascending */
+      int c = 0;
+      for (int r = node * per_node; r < (node + 1) * per_node; ++r)
+        c += holds[(size_t)r * E + e] != 0;
+      int j = pick(u_rank[i], c);
+      int rank = -1;
+      for (int r = node * per_node; r < (node + 1) * per_node; ++r)
+        if (holds[(size_t)r * E + e]) {
+          if (j == 0) {
+            rank = r;
+            break;
+          }
+          --j;
+        }
+      assign_rank[i] = rank;
+    }
+  }
+  return REF_OK;
+}
