@@ -10,7 +10,8 @@ sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                        [--workload deepseek_v3] [--no-cpu-baseline]
-                       [--path flat|two_leg|fp8|capacity] [--gamma 1.25]
+                       [--path flat|two_leg|fp8|capacity|assign]
+                       [--gamma 1.25] [--rho 0.5]
                        [--part-dtype bf16|f32]
 
 --path two_leg times moe_dispatch_combine_nodes instead: the node-level
@@ -20,7 +21,10 @@ at the source).  --path fp8 times moe_dispatch_combine_fp8: the pack
 quantises each row to E4M3 codes with one fp32 scale per 128 elements and the
 combine gathers and dequantises those rows.  --path capacity times
 moe_dispatch_combine_capacity with one level C = ceil(gamma*T*K/E): every
-expert's segment padded to C rows, overflow dropped.
+expert's segment padded to C rows, overflow dropped.  --path assign times
+the gate and moe_assign_tasks on a seeded replica layout (rho*E extra
+replicas), tokens from rank 0, and reports remote-node crossings with and
+without the replicas.
 """
 from __future__ import annotations
 
@@ -128,7 +132,9 @@ def main() -> int:
     ap.add_argument("--fused-only", action="store_true",
                     help="time only the fused call (for profiler runs)")
     ap.add_argument("--path", default="flat",
-                    choices=("flat", "two_leg", "fp8", "capacity"))
+                    choices=("flat", "two_leg", "fp8", "capacity", "assign"))
+    ap.add_argument("--rho", type=float, default=0.5,
+                    help="replica budget of --path assign")
     ap.add_argument("--gamma", type=float, default=1.25,
                     help="capacity factor of --path capacity")
     ap.add_argument("--part-dtype", default="bf16", choices=("bf16", "f32"))
@@ -177,6 +183,9 @@ def main() -> int:
     if args.path == "two_leg":
         return two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out,
                        ws, stream)
+    if args.path == "assign":
+        del send
+        return assign_path(args, w, d, cfg, lg, idx, wt, stream)
     if args.path == "capacity":
         del send
         return capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream)
@@ -555,6 +564,76 @@ def capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream) -> int:
                      "launch_ms": steps_ms[dom],
                      **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
                         for k in kb}},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def assign_path(args, w, d, cfg, lg, idx, wt, stream) -> int:
+    """Time gate + moe_assign_tasks; report crossings; JSON line."""
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    dev = lg.device
+    holds = torch.from_numpy(mi.replica_layout(w.E, w.R, args.rho, 0)).to(dev)
+    un, ur = mi.assign_draws(w.T, w.K, 0)
+    un = torch.from_numpy(un.view(np.int32)).to(dev)
+    ur = torch.from_numpy(ur.view(np.int32)).to(dev)
+    src = torch.zeros(w.T, dtype=torch.int32, device=dev)
+    ar = torch.empty(w.T * w.K, dtype=torch.int32, device=dev)
+    rm = torch.empty(w.T, dtype=torch.int64, device=dev)
+    ws = moe.alloc_assign_workspace(cfg, dev)
+
+    def step():
+        moe.moe_topk_gate(cfg, lg, idx, wt, stream)
+        moe.moe_assign_tasks(cfg, idx, src, holds, un, ur, ar, rm, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if moe.moe_read_device_error(ws) != 0:
+        raise RuntimeError("device reported an input error")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_gate = t_assign = 0.0
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        moe.moe_topk_gate(cfg, lg, idx, wt, stream)
+        ev[1].record(stream)
+        moe.moe_assign_tasks(cfg, idx, src, holds, un, ur, ar, rm, ws, stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_gate += ev[0].elapsed_time(ev[1])
+        t_assign += ev[1].elapsed_time(ev[2])
+    ms_gate, ms_assign = t_gate / args.steps, t_assign / args.steps
+    ms = ms_gate + ms_assign
+    masks = rm.cpu().numpy().view(np.uint64)
+    with_rep = int(sum(bin(int(v)).count("1") for v in masks))
+    # the same tokens with home placement only (no replicas): the remote
+    # nodes of the token's experts
+    per_rank, per_node = w.E // w.R, w.R // w.N
+    home = (idx.view(w.T, w.K).cpu().numpy() // per_rank) // per_node
+    without = int(sum(len(set(r.tolist()) - {0}) for r in home))
+    print(f"bench: assign {ms_assign * 1e3:.1f} us, crossings {with_rep} "
+          f"with replicas vs {without} without", file=sys.stderr, flush=True)
+    T, K = w.T, w.K
+    by = T * (4 * K + 8 * K + 4 + 4 * K + 8) + w.R * w.E + 8 * w.E
+    result = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": w.name, "path": "assign", "T": T, "E": w.E,
+                   "K": K, "R": w.R, "N": w.N, "rho": args.rho,
+                   "src_rank": 0, "seed": w.seed},
+        "steps_ms": {"gate": ms_gate, "assign": ms_assign},
+        "crossings": {"with_replicas": with_rep, "home_only": without,
+                      "ratio": with_rep / max(without, 1)},
+        "roofline": {"kernel": "assign", "bound": "alu",
+                     "achieved": T / (ms_assign * 1e-3) / 1e6,
+                     "peak": None, "unit": "Mtokens/s", "frac": None,
+                     "traffic": None, "alg_bytes_per_launch": by,
+                     "launch_ms": ms_assign},
     }
     print(json.dumps(result), flush=True)
     return 0

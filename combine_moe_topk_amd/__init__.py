@@ -10,7 +10,8 @@ and the node-level two-leg path :func:`moe_dispatch_pack_nodes`,
 dispatch :func:`moe_dispatch_pack_fp8`, :func:`moe_combine_fp8`,
 :func:`moe_dispatch_combine_fp8`, and the capacity-padded / bucketed layout
 :func:`moe_dispatch_layout_capacity`, :func:`moe_dispatch_pack_capacity`,
-:func:`moe_combine_capacity`, :func:`moe_dispatch_combine_capacity`.
+:func:`moe_combine_capacity`, :func:`moe_dispatch_combine_capacity`, and the
+communication-aware task assignment :func:`moe_assign_tasks`.
 """
 from ._lib import (  # noqa: F401
     LAYOUT_FIELDS, Layout, MoeError, MOE_BF16, MOE_DEVERR_DUP_EXPERT,
@@ -28,4 +29,6 @@ from ._lib import (  # noqa: F401
     alloc_capacity_layout, alloc_capacity_workspace,
     moe_dispatch_layout_capacity, moe_dispatch_pack_capacity,
     moe_combine_capacity, moe_dispatch_combine_capacity,
+    MOE_DEVERR_NO_REPLICA, MOE_DEVERR_SRC_RANK, alloc_assign_workspace,
+    moe_assign_tasks,
 )

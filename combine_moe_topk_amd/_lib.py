@@ -24,6 +24,8 @@ MOE_ELAUNCH = -4
 
 MOE_DEVERR_EXPERT_RANGE = 0x1
 MOE_DEVERR_DUP_EXPERT = 0x2
+MOE_DEVERR_NO_REPLICA = 0x4
+MOE_DEVERR_SRC_RANK = 0x8
 
 MOE_F32 = 0
 MOE_BF16 = 1
@@ -129,6 +131,9 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_combine_capacity": (ctypes.c_int, [
                 _CFG, _P, _P, _P, _P, _P, _I32P, ctypes.c_int32, _CAP, _P, _P,
                 _P, ctypes.c_size_t, _P]),
+            "moe_assign_workspace_bytes": (ctypes.c_size_t, [_CFG]),
+            "moe_assign_tasks": (ctypes.c_int, [
+                _CFG, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "moe_read_device_error": (ctypes.c_int, [_P, _P,
                                                      ctypes.POINTER(ctypes.c_int32),
                                                      ctypes.c_int]),
@@ -552,6 +557,38 @@ def moe_dispatch_combine_capacity(cfg: moe_cfg, x: torch.Tensor,
         _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
         "moe_dispatch_combine_capacity")
+
+
+# ---- communication-aware task assignment -----------------------------------
+
+def alloc_assign_workspace(cfg: moe_cfg, device="cuda",
+                           stream=None) -> torch.Tensor:
+    n = lib().moe_assign_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise MoeError(moe_validate_cfg(cfg), "moe_assign_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    moe_workspace_init(ws, stream)
+    return ws
+
+
+def moe_assign_tasks(cfg: moe_cfg, topk_idx: torch.Tensor,
+                     src_rank: torch.Tensor, holds: torch.Tensor,
+                     u_node: torch.Tensor, u_rank: torch.Tensor,
+                     assign_rank: torch.Tensor, remote_mask: torch.Tensor,
+                     ws: torch.Tensor, stream=None) -> None:
+    """holds: uint8 [R, E]; u_node/u_rank: int32 views of uint32 draws;
+    remote_mask: int64 (bit n = node n)."""
+    if holds.numel() != cfg.R * cfg.E:
+        raise ValueError("holds must be [R, E]")
+    _check(lib().moe_assign_tasks(
+        ctypes.byref(cfg), _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(src_rank, torch.int32, "src_rank"),
+        _ptr(holds, torch.uint8, "holds"), _ptr(u_node, torch.int32, "u_node"),
+        _ptr(u_rank, torch.int32, "u_rank"),
+        _ptr(assign_rank, torch.int32, "assign_rank"),
+        _ptr(remote_mask, torch.int64, "remote_mask"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+        "moe_assign_tasks")
 
 
 def moe_read_device_error(ws: torch.Tensor, clear: bool = True,

@@ -421,6 +421,32 @@ int moe_dispatch_combine_capacity(const moe_cfg *cfg, const void *x,
   return launch_status(e);
 }
 
+size_t moe_assign_workspace_bytes(const moe_cfg *cfg) {
+  if (validate(cfg) != MOE_OK) return 0;
+  return moe::assign_ws_bytes(*cfg);
+}
+
+int moe_assign_tasks(const moe_cfg *cfg, const int32_t *topk_idx,
+                     const int32_t *src_rank, const uint8_t *holds,
+                     const uint32_t *u_node, const uint32_t *u_rank,
+                     int32_t *assign_rank, uint64_t *remote_mask, void *ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if (!moe::assign_ok(*cfg)) return MOE_EUNSUPPORTED;
+  if (!holds) return MOE_EINVAL;
+  if (cfg->T > 0 && (!topk_idx || !src_rank || !u_node || !u_rank ||
+                     !assign_rank || !remote_mask))
+    return MOE_EINVAL;
+  if (remote_mask && !aligned(remote_mask, 8)) return MOE_EUNSUPPORTED;
+  if (!ws) return MOE_EWORKSPACE;
+  if (!aligned(ws, 256)) return MOE_EUNSUPPORTED;
+  if (ws_bytes < moe::assign_ws_bytes(*cfg)) return MOE_EWORKSPACE;
+  return launch_status(moe::launch_assign(*cfg, topk_idx, src_rank, holds,
+                                          u_node, u_rank, assign_rank,
+                                          remote_mask, ws, stream));
+}
+
 int moe_read_device_error(const void *ws, hipStream_t stream,
                           int32_t *host_code, int clear) {
   if (!ws || !host_code) return MOE_EINVAL;

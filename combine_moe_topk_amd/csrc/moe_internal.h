@@ -110,4 +110,14 @@ hipError_t launch_pack_capacity(const moe_cfg &c, const void *x,
                                 const int32_t *row_src, int n_rows,
                                 void *send, hipStream_t stream);
 
+// Communication-aware task assignment (assign.hip).
+size_t assign_ws_bytes(const moe_cfg &c);
+bool assign_ok(const moe_cfg &c);  // R/N <= 64 ranks per node
+
+hipError_t launch_assign(const moe_cfg &c, const int32_t *topk_idx,
+                         const int32_t *src_rank, const uint8_t *holds,
+                         const uint32_t *u_node, const uint32_t *u_rank,
+                         int32_t *assign_rank, uint64_t *remote_mask, void *ws,
+                         hipStream_t stream);
+
 }  // namespace moe

@@ -64,6 +64,8 @@ extern "C" {
 /* ---- device-detected input errors (bits of the workspace error word) --- */
 #define MOE_DEVERR_EXPERT_RANGE 0x1 /* a topk_idx entry outside [0, E)      */
 #define MOE_DEVERR_DUP_EXPERT 0x2   /* one token lists an expert twice      */
+#define MOE_DEVERR_NO_REPLICA 0x4   /* an expert with no replica anywhere   */
+#define MOE_DEVERR_SRC_RANK 0x8     /* a source rank outside [0, R)         */
 
 /* ---- element types ----------------------------------------------------- */
 #define MOE_F32 0  /* IEEE binary32                                         */
@@ -368,6 +370,35 @@ int moe_dispatch_combine_capacity(const moe_cfg *cfg, const void *x,
                                   const moe_capacity_layout *layout,
                                   void *send, void *out, void *ws,
                                   size_t ws_bytes, hipStream_t stream);
+
+/* ---- communication-aware task assignment ------------------------------
+ * "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
+ * Training", Section 3.3.  The R ranks of cfg sit on N nodes, R/N contiguous
+ * ranks a node; holds[r*E + e] != 0 when rank r holds a replica of expert e
+ * (any number of replicas per expert).  For token t from source rank
+ * src_rank[t] (node sn):
+ *   - a selected expert with a replica on node sn runs on node sn;
+ *   - for the others, remote_mask[t] = the smallest set of remote nodes that
+ *     holds each of them (bit n = node n); among sets of equal size the one
+ *     with the smallest mask value;
+ *   - each such expert runs on node number floor(u_node * c / 2^32) (in
+ *     ascending order) of the c nodes of remote_mask[t] holding it;
+ *   - assign_rank[t*K+k] = rank number floor(u_rank * c / 2^32) of the c
+ *     ranks of that node holding the expert (ascending).
+ * u_node, u_rank: [T*K] uint32 draws supplied by the caller (uniform draws
+ * give the random and uniform choices of the page).  An expert id outside
+ * [0, E), an expert without replica or a source rank outside [0, R) sets
+ * the matching MOE_DEVERR_* bit, and that token's ranks are -1.  Needs at
+ * most 64 ranks per node (MOE_EUNSUPPORTED otherwise). */
+
+/* Workspace bytes of moe_assign_tasks (0 when cfg is invalid).  Host only. */
+size_t moe_assign_workspace_bytes(const moe_cfg *cfg);
+
+int moe_assign_tasks(const moe_cfg *cfg, const int32_t *topk_idx,
+                     const int32_t *src_rank, const uint8_t *holds,
+                     const uint32_t *u_node, const uint32_t *u_rank,
+                     int32_t *assign_rank, uint64_t *remote_mask, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* Copy the workspace error word (MOE_DEVERR_* bits, 0 when clean) to
  * *host_code after all work queued on `stream`; synchronises `stream`.  When

@@ -178,3 +178,13 @@ def test_capacity_entry_points_validate_on_host():
     assert moe.moe_fp8_row_bytes(7168, 128) == 7168 + 224
     assert moe.moe_fp8_row_bytes(256, 128) == 272
     assert moe.moe_fp8_row_bytes(100, 32) == 0
+
+
+def test_assign_entry_point_validates_on_host():
+    assert "moe_assign_tasks" in declared_functions()
+    c = cfg()
+    assert moe.lib().moe_assign_workspace_bytes(ctypes.byref(c)) == \
+        256 + 256 * 8 + 256 * 8 * 8
+    lib = moe.lib()
+    assert lib.moe_assign_tasks(ctypes.byref(c), None, None, None, None, None,
+                                None, None, None, 0, None) == moe.MOE_EINVAL
