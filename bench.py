@@ -44,9 +44,11 @@ import moe_inputs as mi  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1 MI355X"
+# sources whose text decides each kernel's memory traffic
 KERNEL_SOURCES = {
-    "pack": "combine_moe_topk_amd/csrc/pack.hip",
-    "combine": "combine_moe_topk_amd/csrc/combine.hip",
+    "pack": ["combine_moe_topk_amd/csrc/pack.hip"],
+    "combine": ["combine_moe_topk_amd/csrc/combine.hip",
+                "combine_moe_topk_amd/csrc/row_io.h"],
 }
 
 
@@ -78,9 +80,12 @@ def two_leg_kernel_bytes(w: mi.Workload, D: int, pb: int) -> dict:
     }
 
 
-def source_digest(path: str) -> str:
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(kernel: str, workload: str):
