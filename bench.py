@@ -125,6 +125,90 @@ def cpu_baseline(w: mi.Workload, d: dict, sample_tokens: int) -> dict:
                       f"{dt:.2f} s"}
 
 
+def _pct(a, q):
+    return float(np.percentile(np.asarray(a), q))
+
+
+def extras(w, step, stream, alg, dev) -> dict:
+    """Outside the timed region: per-step spread (warm), steps after flushing
+    the last-level cache (cold), a device-to-device copy ceiling, and the
+    clocks and versions of this run."""
+    import subprocess
+
+    import torch
+
+    n = 20
+    # warm: back-to-back steps, one event pair each
+    warm = []
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        warm.append((a, b))
+    torch.cuda.synchronize()
+    warm = [a.elapsed_time(b) for a, b in warm]
+    # cold: 1 GiB written between steps evicts the 256 MB last-level cache
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(n):
+        flush.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    cold = [a.elapsed_time(b) for a, b in cold]
+    del flush
+    # copy ceiling: 2 GiB device-to-device copies
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 31) * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+
+    def run(cmd):
+        try:
+            return subprocess.run(cmd, capture_output=True, text=True,
+                                  timeout=20).stdout.strip()
+        except (OSError, subprocess.SubprocessError):
+            return None
+
+    clocks = run(["rocm-smi", "--showclocks", "--json"])
+    try:  # keep the current engine and memory clocks of card 0 only
+        card = next(iter(json.loads(clocks).values()))
+        clocks = {k: v for k, v in card.items()
+                  if k.startswith(("sclk", "mclk", "fclk"))}
+    except (TypeError, ValueError, StopIteration, AttributeError):
+        pass
+    ver = None
+    try:
+        ver = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    med_w = _pct(warm, 50)
+    return {
+        "warm_ms": {"p10": _pct(warm, 10), "p50": med_w, "p90": _pct(warm, 90)},
+        "cold_ms": {"p10": _pct(cold, 10), "p50": _pct(cold, 50),
+                    "p90": _pct(cold, 90)},
+        "copy_ceiling_gbps": copy_gbps,
+        "frac_of_copy_ceiling": alg / (med_w * 1e-3) / 1e9 / copy_gbps,
+        "rocm": ver, "torch": torch.__version__,
+        "clocks": clocks,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +220,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--fused-only", action="store_true",
                     help="time only the fused call (for profiler runs)")
+    ap.add_argument("--layout-tile", type=int, default=0,
+                    help="tokens per layout workgroup (0: library default)")
     ap.add_argument("--path", default="flat",
                     choices=("flat", "two_leg", "fp8", "capacity", "assign"))
     ap.add_argument("--rho", type=float, default=0.5,
@@ -143,6 +229,9 @@ def main() -> int:
     ap.add_argument("--gamma", type=float, default=1.25,
                     help="capacity factor of --path capacity")
     ap.add_argument("--part-dtype", default="bf16", choices=("bf16", "f32"))
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-step distribution, cold-cache steps "
+                         "and the copy ceiling")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run 3 plain device copies of this many MiB "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -175,7 +264,7 @@ def main() -> int:
     rows = torch.float32 if w.x_dtype == mi.F32 else torch.bfloat16
     odt = torch.float32 if w.out_dtype == mi.F32 else torch.bfloat16
     cfg = moe.make_cfg(w.T, w.H, w.E, w.K, w.R, w.N, w.x_dtype, w.out_dtype,
-                       w.renorm)
+                       w.renorm, args.layout_tile)
     x, lg = to_dev(d["x"]), to_dev(d["logits"])
     scale = None if d["expert_scale"] is None else to_dev(d["expert_scale"])
     idx = torch.empty(w.T * w.K, dtype=torch.int32, device=dev)
@@ -289,6 +378,9 @@ def main() -> int:
         torch.cuda.synchronize()
         result["copy_calib_bytes"] = nb
         del src, dst
+
+    if not args.fused_only and not args.no_extras:
+        result["extras"] = extras(w, step, stream, alg, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)

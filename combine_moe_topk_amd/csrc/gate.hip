@@ -8,13 +8,18 @@
 // create ties that rounding of exp() would); equal logits go to the lower
 // expert index; -0.0 ranks equal to +0.0.
 //
-// Layout: a group of G lanes (G a power of two, 8..64) owns one token.  Lane
-// `sub` of the group holds the logits of experts sub, sub+G, sub+2G, ... as
-// 64-bit keys (order-preserving logit bits << 32 | ~expert), so one unsigned
-// max picks "larger logit, then lower index".  K rounds of (per-lane max,
-// butterfly max over the group, winner cleared) select the experts in
-// descending order; lane k of the group keeps round k's winner.  Row loads are
-// coalesced: G consecutive floats per group per load.
+// Layout: a group of G lanes (16, 32 or 64) owns one token.  Lane `sub` of
+// the group holds the logits of experts sub, sub+G, sub+2G, ... as 32-bit
+// order-preserving keys (larger key = larger logit) and caches its best key
+// and that key's lowest expert index.  A round takes the group maximum of the
+// cached keys, then the group minimum of the expert indices holding it, so
+// "larger logit, then lower index" wins; the winning lane clears that key and
+// recomputes its cache.  Group reductions are DPP inside 16-lane rows
+// (quad_perm, half-mirror, mirror: every lane of the row ends with the row's
+// result) and readlane across rows, with no LDS permutes.  Per token and
+// round the cache update costs about 5E/64 lane-instructions whatever G is,
+// while the reduction is shared by the 64/G tokens of a wave, so G is the
+// smallest width that keeps at most 64 keys per lane and K <= G.
 #include "moe_internal.h"
 
 namespace moe {
@@ -31,59 +36,135 @@ __device__ __forceinline__ float from_order_bits(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror.  Together they reduce a 16-lane row into every lane.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF,
+                                               false);
+}
+
+// Combine the four 16-lane rows' results for groups of G = 32 or 64 lanes.
+template <int G, bool MAX>
+__device__ __forceinline__ uint32_t across_rows(uint32_t v) {
+  if constexpr (G == 16) {
+    return v;
+  } else {
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0);
+    const uint32_t r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32);
+    const uint32_t r3 = __builtin_amdgcn_readlane(v, 48);
+    const uint32_t a = MAX ? (r0 > r1 ? r0 : r1) : (r0 < r1 ? r0 : r1);
+    const uint32_t b = MAX ? (r2 > r3 ? r2 : r3) : (r2 < r3 ? r2 : r3);
+    if constexpr (G == 32) {
+      return (threadIdx.x & 32) ? b : a;
+    } else {
+      return MAX ? (a > b ? a : b) : (a < b ? a : b);
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  v = max(v, dpp<kDppQuadXor1>(v));
+  v = max(v, dpp<kDppQuadXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  return across_rows<G, true>(v);
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_min(uint32_t v) {
+  v = min(v, dpp<kDppQuadXor1>(v));
+  v = min(v, dpp<kDppQuadXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  v = min(v, dpp<kDppMirror>(v));
+  return across_rows<G, false>(v);
+}
+
+template <int G>
+__device__ __forceinline__ double group_sum_f64(double v) {
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, G);
+  return v;
+}
+
+// Best key of the lane and the position of its first occurrence.
+template <int C>
+__device__ __forceinline__ void lane_best(const uint32_t *key, uint32_t &best,
+                                          int &at) {
+  best = key[0];
+  at = 0;
+#pragma unroll
+  for (int j = 1; j < C; ++j)
+    if (key[j] > best) {  // strict: the lowest j (lowest expert) keeps a tie
+      best = key[j];
+      at = j;
+    }
+}
+
+// C keys per lane.  Keys of experts >= E are 0, below every real key (the
+// smallest finite logit has key 0x00800000); a taken key becomes 0 as well.
 template <int G, int C>
 __global__ __launch_bounds__(256) void gate_kernel(
     const float *__restrict__ logits, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, int T, int E, int K, int renorm) {
   constexpr int kTokensPerBlock = 256 / G;
   const int sub = threadIdx.x & (G - 1);
-  const int t = blockIdx.x * kTokensPerBlock + threadIdx.x / G;
-  if (t >= T) return;  // whole groups leave together
+  int t = blockIdx.x * kTokensPerBlock + threadIdx.x / G;
+  // groups past the last token compute on token T-1 and store nothing, so
+  // every lane of a wave runs the DPP reductions (whole waves leave only
+  // when the wave's first token is past the end)
+  const bool live = t < T;
+  if (blockIdx.x * kTokensPerBlock + (threadIdx.x & ~63) / G >= T) return;
+  if (!live) t = T - 1;
   const float *row = logits + (size_t)t * E;
 
-  uint64_t key[C];
+  uint32_t key[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int e = sub + j * G;
-    key[j] = 0;  // below every real key
-    if (e < E)
-      key[j] = ((uint64_t)order_bits(row[e]) << 32) |
-               (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    key[j] = e < E ? order_bits(row[e]) : 0u;
   }
+  uint32_t best;
+  int at;
+  lane_best<C>(key, best, at);
 
   int my_e = 0;
   float my_l = 0.0f;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int j = 1; j < C; ++j) best = key[j] > best ? key[j] : best;
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) {
-      const uint64_t o = __shfl_xor(best, off, G);
-      best = o > best ? o : best;
-    }
-#pragma unroll
-    for (int j = 0; j < C; ++j)
-      if (key[j] == best) key[j] = 0;  // keys are unique: one owner
+    const uint32_t m = group_max<G>(best);
+    const uint32_t cand = best == m ? (uint32_t)(sub + at * G) : 0xFFFFFFFFu;
+    const uint32_t win = group_min<G>(cand);
     if (sub == k) {
-      my_e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      my_l = from_order_bits((uint32_t)(best >> 32));
+      my_e = (int)win;
+      my_l = from_order_bits(m);
+    }
+    if (cand == win) {  // the one lane holding the winner
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+        if (j == at) key[j] = 0u;
+      lane_best<C>(key, best, at);
     }
   }
 
   // Weights in fp64: exp(l_k - l_max) / sum, rounded once to fp32.
-  const double m = (double)__shfl(my_l, 0, G);
-  const double ex = (sub < K) ? exp((double)my_l - m) : 0.0;
+  const double mx = (double)__shfl(my_l, 0, G);
+  const double ex = (sub < K) ? exp((double)my_l - mx) : 0.0;
   double denom = 0.0;
   if (renorm) {
     denom = ex;
   } else {
-    for (int e = sub; e < E; e += G) denom += exp((double)row[e] - m);
+    for (int e = sub; e < E; e += G) denom += exp((double)row[e] - mx);
   }
-#pragma unroll
-  for (int off = G / 2; off > 0; off >>= 1) denom += __shfl_xor(denom, off, G);
+  denom = group_sum_f64<G>(denom);
 
-  if (sub < K) {
+  if (live && sub < K) {
     topk_idx[(size_t)t * K + sub] = my_e;
     topk_w[(size_t)t * K + sub] = (float)(ex / denom);
   }
@@ -113,17 +194,12 @@ hipError_t launch_g(int C, const float *logits, int32_t *idx, float *w,
     case 2: return launch_gc<G, 2>(logits, idx, w, T, E, K, renorm, s);
     case 4: return launch_gc<G, 4>(logits, idx, w, T, E, K, renorm, s);
     case 8: return launch_gc<G, 8>(logits, idx, w, T, E, K, renorm, s);
-    default: break;
+    case 16: return launch_gc<G, 16>(logits, idx, w, T, E, K, renorm, s);
+    case 32: return launch_gc<G, 32>(logits, idx, w, T, E, K, renorm, s);
+    case 48: return launch_gc<G, 48>(logits, idx, w, T, E, K, renorm, s);
+    case 64: return launch_gc<G, 64>(logits, idx, w, T, E, K, renorm, s);
+    default: return hipErrorInvalidValue;
   }
-  if constexpr (G == 64) {
-    switch (C) {
-      case 16: return launch_gc<64, 16>(logits, idx, w, T, E, K, renorm, s);
-      case 32: return launch_gc<64, 32>(logits, idx, w, T, E, K, renorm, s);
-      case 64: return launch_gc<64, 64>(logits, idx, w, T, E, K, renorm, s);
-      default: break;
-    }
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -131,15 +207,14 @@ hipError_t launch_g(int C, const float *logits, int32_t *idx, float *w,
 hipError_t launch_gate(const moe_cfg &c, const float *logits,
                        int32_t *topk_idx, float *topk_w, hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
-  // About 8 logits per lane; a group is never narrower than K.
-  int G = pow2_ceil((c.E + 7) / 8);
-  G = G < 8 ? 8 : (G > 64 ? 64 : G);
-  const int gk = pow2_ceil(c.K);
-  if (G < gk) G = gk;
-  const int C = pow2_ceil((c.E + G - 1) / G);
+  // smallest group with at most 64 keys per lane and K <= G
+  int G = 16;
+  while (G < 64 && ((c.E + G - 1) / G > 64 || G < c.K)) G <<= 1;
+  const int need = (c.E + G - 1) / G;  // keys per lane, <= 64
+  int C = need <= 2 ? pow2_ceil(need) : (need <= 32 ? pow2_ceil(need) : (need <= 48 ? 48 : 64));
+  if (C < 1) C = 1;
   const int renorm = (c.flags & MOE_F_NO_RENORM) ? 0 : 1;
   switch (G) {
-    case 8: return launch_g<8>(C, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
     case 16: return launch_g<16>(C, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
     case 32: return launch_g<32>(C, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
     case 64: return launch_g<64>(C, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);

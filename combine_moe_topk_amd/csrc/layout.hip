@@ -129,24 +129,24 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
   const int cols = E + R + N;
   int32_t *tot = sm32;              // [cols]
   int32_t *eoff = sm32 + cols;      // [E + 1]
-  // Column-wise exclusive prefix over the tiles, in place.
+  // Column-wise exclusive prefix over the tiles, in place.  A thread owns
+  // a column and takes its rows 16 at a time: the 16 loads are issued
+  // before any store (stores to the table would otherwise order every later
+  // load behind them), so a chunk costs one memory round trip.
+  constexpr int kChunk = 16;
   for (int c = threadIdx.x; c < cols; c += blockDim.x) {
     int run = 0;
-    int b = 0;
-    for (; b + 4 <= nblocks; b += 4) {
-      int32_t *p = table + (size_t)b * cols + c;
-      const int v0 = p[0], v1 = p[cols], v2 = p[2 * cols], v3 = p[3 * cols];
-      p[0] = run;
-      p[cols] = run + v0;
-      p[2 * cols] = run + v0 + v1;
-      p[3 * cols] = run + v0 + v1 + v2;
-      run += v0 + v1 + v2 + v3;
-    }
-    for (; b < nblocks; ++b) {
-      int32_t *p = table + (size_t)b * cols + c;
-      const int v = *p;
-      *p = run;
-      run += v;
+    for (int b0 = 0; b0 < nblocks; b0 += kChunk) {
+      int32_t *p = table + (size_t)b0 * cols + c;
+      const int n = min(kChunk, nblocks - b0);
+      int v[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) v[j] = j < n ? p[(size_t)j * cols] : 0;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        if (j < n) p[(size_t)j * cols] = run;
+        run += v[j];
+      }
     }
     tot[c] = run;
   }
