@@ -10,16 +10,19 @@
 //
 // Layout: a group of G lanes (16, 32 or 64) owns one token.  Lane `sub` of
 // the group holds the logits of experts sub, sub+G, sub+2G, ... as 32-bit
-// order-preserving keys (larger key = larger logit) and caches its best key
-// and that key's lowest expert index.  A round takes the group maximum of the
-// cached keys, then the group minimum of the expert indices holding it, so
-// "larger logit, then lower index" wins; the winning lane clears that key and
-// recomputes its cache.  Group reductions are DPP inside 16-lane rows
-// (quad_perm, half-mirror, mirror: every lane of the row ends with the row's
-// result) and readlane across rows, with no LDS permutes.  Per token and
-// round the cache update costs about 5E/64 lane-instructions whatever G is,
-// while the reduction is shared by the 64/G tokens of a wave, so G is the
-// smallest width that keeps at most 64 keys per lane and K <= G.
+// order-preserving keys (larger key = larger logit) and a sorted cache of its
+// D best (key, position) pairs, ordered by key descending, position
+// ascending.  A round takes the group maximum of the cache heads, then the
+// group minimum of the expert indices holding it, so "larger logit, then
+// lower index" wins; the winning lane pops its head.  A lane whose cache runs
+// empty refills it with the D best pairs strictly after the last one it gave
+// out (in the same order), so no key is ever cleared; refills run under a
+// wave-uniform branch and are rare (a lane empties only after D wins).
+// Group reductions are DPP inside 16-lane rows (quad_perm, half-mirror,
+// mirror: every lane of the row ends with the row's result) and readlane
+// across rows, with no LDS permutes.  G is the smallest width that keeps at
+// most 64 keys per lane and K <= G (the reductions are then shared by the
+// 64/G tokens of a wave).
 #include "moe_internal.h"
 
 namespace moe {
@@ -94,22 +97,72 @@ __device__ __forceinline__ double group_sum_f64(double v) {
   return v;
 }
 
-// Best key of the lane and the position of its first occurrence.
-template <int C>
-__device__ __forceinline__ void lane_best(const uint32_t *key, uint32_t &best,
-                                          int &at) {
-  best = key[0];
-  at = 0;
+constexpr int kCache = 4;  // D: cached (key, position) pairs per lane
+
+// Sorted cache of a lane's best keys (key descending, position ascending).
+struct Cache {
+  uint32_t key[kCache];
+  int pos[kCache];
+  int n;          // valid entries
+  bool more;      // keys after the cache may remain
+  uint32_t lk;    // last key given out (refills start strictly after it)
+  int lp;         //   and its position
+
+  // Insert (k, j); j comes in ascending order, so an equal key stays behind.
+  __device__ __forceinline__ void insert(uint32_t k, int j) {
+    if (k <= key[kCache - 1]) return;
+    key[kCache - 1] = k;
+    pos[kCache - 1] = j;
 #pragma unroll
-  for (int j = 1; j < C; ++j)
-    if (key[j] > best) {  // strict: the lowest j (lowest expert) keeps a tie
-      best = key[j];
-      at = j;
+    for (int i = kCache - 1; i > 0; --i) {
+      if (key[i] > key[i - 1]) {
+        const uint32_t tk = key[i];
+        key[i] = key[i - 1];
+        key[i - 1] = tk;
+        const int tp = pos[i];
+        pos[i] = pos[i - 1];
+        pos[i - 1] = tp;
+      }
     }
-}
+  }
+
+  // The D best pairs among those after (lk, lp); with first, all of them.
+  template <int C>
+  __device__ __forceinline__ void fill(const uint32_t *keys, bool first) {
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) {
+      key[i] = 0u;
+      pos[i] = 0;
+    }
+    int found = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const uint32_t k = keys[j];
+      const bool after = first || k < lk || (k == lk && j > lp);
+      if (k != 0u && after) {
+        insert(k, j);
+        ++found;
+      }
+    }
+    n = found < kCache ? found : kCache;
+    more = found > kCache;
+  }
+
+  __device__ __forceinline__ void pop() {
+    lk = key[0];
+    lp = pos[0];
+#pragma unroll
+    for (int i = 0; i < kCache - 1; ++i) {
+      key[i] = key[i + 1];
+      pos[i] = pos[i + 1];
+    }
+    key[kCache - 1] = 0u;
+    --n;
+  }
+};
 
 // C keys per lane.  Keys of experts >= E are 0, below every real key (the
-// smallest finite logit has key 0x00800000); a taken key becomes 0 as well.
+// smallest finite logit has key 0x00800000), and never enter a cache.
 template <int G, int C>
 __global__ __launch_bounds__(256) void gate_kernel(
     const float *__restrict__ logits, int32_t *__restrict__ topk_idx,
@@ -131,25 +184,28 @@ __global__ __launch_bounds__(256) void gate_kernel(
     const int e = sub + j * G;
     key[j] = e < E ? order_bits(row[e]) : 0u;
   }
-  uint32_t best;
-  int at;
-  lane_best<C>(key, best, at);
+  Cache cache;
+  cache.lk = 0u;
+  cache.lp = 0;
+  cache.fill<C>(key, true);
 
   int my_e = 0;
   float my_l = 0.0f;
   for (int k = 0; k < K; ++k) {
-    const uint32_t m = group_max<G>(best);
-    const uint32_t cand = best == m ? (uint32_t)(sub + at * G) : 0xFFFFFFFFu;
+    const uint32_t head = cache.n > 0 ? cache.key[0] : 0u;
+    const uint32_t m = group_max<G>(head);
+    const uint32_t cand = (cache.n > 0 && head == m)
+                              ? (uint32_t)(sub + cache.pos[0] * G)
+                              : 0xFFFFFFFFu;
     const uint32_t win = group_min<G>(cand);
     if (sub == k) {
       my_e = (int)win;
       my_l = from_order_bits(m);
     }
-    if (cand == win) {  // the one lane holding the winner
-#pragma unroll
-      for (int j = 0; j < C; ++j)
-        if (j == at) key[j] = 0u;
-      lane_best<C>(key, best, at);
+    if (cand == win) cache.pop();  // the one lane holding the winner
+    const bool refill = cache.n == 0 && cache.more;
+    if (__any(refill)) {
+      if (refill) cache.fill<C>(key, false);
     }
   }
 
