@@ -20,7 +20,9 @@
 //   rank of (t, e) among earlier tile rows = popcount(bitmap & lanes-below)
 //                                            + popcounts of earlier waves
 // which is exactly the token-ascending order inside each expert, with no
-// sorting and no order-dependent atomics.  Three launches:
+// sorting and no order-dependent atomics.  When all tokens fit in one tile,
+// one workgroup does everything (layout_single_kernel).  Otherwise three
+// launches:
 //   count: per-tile column counts (experts | ranks | nodes) + node masks
 //   scan : one workgroup turns the count table into per-tile exclusive
 //          prefixes, totals, expert/rank/node offsets
@@ -248,6 +250,114 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   }
 }
 
+// The whole layout in one workgroup when every token fits in one tile (the
+// decode case): the same LDS bitmaps give the counts, the offsets (scanned in
+// LDS) and the ranks, in one launch instead of three.
+__global__ __launch_bounds__(1024) void layout_single_kernel(
+    const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
+    int per_rank, int per_node_e, int32_t *__restrict__ expert_count,
+    int32_t *__restrict__ expert_off, int32_t *__restrict__ rank_count,
+    int32_t *__restrict__ rank_off, int32_t *__restrict__ rank_token_count,
+    uint64_t *__restrict__ node_mask, int32_t *__restrict__ node_count,
+    int32_t *__restrict__ node_off, int32_t *__restrict__ node_slot,
+    int32_t *__restrict__ slot_pos, int32_t *__restrict__ row_src,
+    int32_t *__restrict__ err) {
+  extern __shared__ uint64_t bm[];  // [W][cols], then the int32 arrays
+  const int cols = E + R + N;
+  const int W = blockDim.x / kWave;
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  int32_t *tot = (int32_t *)(bm + (size_t)W * cols);  // [cols]
+  int32_t *eoff = tot + cols;                          // [E + 1]
+  int32_t *noff = eoff + E + 1;                        // [N + 1]
+  for (int i = threadIdx.x; i < W * cols; i += blockDim.x) bm[i] = 0;
+  __syncthreads();
+
+  const int t = threadIdx.x;
+  const uint64_t bit = 1ull << lane;
+  const uint64_t below = bit - 1;
+  uint64_t *mine = bm + (size_t)w * cols;
+  uint64_t mask = 0;
+  int bad = 0;
+  if (t < T) {
+    const int32_t *row = idx + (size_t)t * K;
+    for (int k = 0; k < K; ++k) {
+      const int e = row[k];
+      if ((unsigned)e >= (unsigned)E) {
+        bad |= MOE_DEVERR_EXPERT_RANGE;
+        continue;
+      }
+      const uint64_t old = atomicOr((unsigned long long *)&mine[e], bit);
+      if (old & bit) bad |= MOE_DEVERR_DUP_EXPERT;
+      atomicOr((unsigned long long *)&mine[E + e / per_rank], bit);
+      mask |= 1ull << (e / per_node_e);
+    }
+    for (uint64_t m = mask; m; m &= m - 1)
+      atomicOr((unsigned long long *)&mine[E + R + __ffsll((long long)m) - 1],
+               bit);
+    if (node_mask) node_mask[t] = mask;
+  }
+  raise_error(err, bad);
+  __syncthreads();
+
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) {
+    int s = 0;
+    for (int v = 0; v < W; ++v) s += __popcll(bm[(size_t)v * cols + c]);
+    tot[c] = s;
+  }
+  __syncthreads();
+  block_exclusive_scan(tot, E, eoff);  // ends with a barrier
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    expert_count[e] = tot[e];
+    expert_off[e] = eoff[e];
+  }
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    rank_off[r] = eoff[r * per_rank];
+    rank_count[r] = eoff[(r + 1) * per_rank] - eoff[r * per_rank];
+    if (rank_token_count) rank_token_count[r] = tot[E + r];
+  }
+  if (threadIdx.x == 0) {
+    expert_off[E] = eoff[E];
+    rank_off[R] = eoff[E];
+    int run = 0;
+    for (int n = 0; n < N; ++n) {
+      noff[n] = run;
+      if (node_count) node_count[n] = tot[E + R + n];
+      if (node_off) node_off[n] = run;
+      run += tot[E + R + n];
+    }
+    noff[N] = run;
+    if (node_off) node_off[N] = run;
+  }
+  __syncthreads();
+
+  if (t >= T) return;
+  const int32_t *row = idx + (size_t)t * K;
+  for (int k = 0; k < K; ++k) {
+    const size_t i = (size_t)t * K + k;
+    const int e = row[k];
+    if ((unsigned)e >= (unsigned)E) {
+      slot_pos[i] = -1;
+      continue;
+    }
+    int s = eoff[e] + __popcll(mine[e] & below);
+    for (int v = 0; v < w; ++v) s += __popcll(bm[(size_t)v * cols + e]);
+    slot_pos[i] = s;
+    row_src[s] = (int32_t)i;
+  }
+  if (node_slot) {
+    for (int n = 0; n < N; ++n) {
+      int s = -1;
+      if (mask >> n & 1) {
+        s = noff[n] + __popcll(mine[E + R + n] & below);
+        for (int v = 0; v < w; ++v)
+          s += __popcll(bm[(size_t)v * cols + E + R + n]);
+      }
+      node_slot[(size_t)t * N + n] = s;
+    }
+  }
+}
+
 }  // namespace
 
 LayoutGeom layout_geom(const moe_cfg &c) {
@@ -279,6 +389,22 @@ hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
   const int per_node_e = c.E / c.N;
   const int threads = g.tile_tokens;
 
+  if (g.nblocks == 1) {
+    // every token in one tile: one workgroup does the whole layout
+    const int waves = (c.T + kWave - 1) / kWave;
+    const size_t lds = (size_t)waves * g.cols * 8 +
+                       (size_t)(g.cols + c.E + 1 + c.N + 1) * 4;
+    if (lds <= (size_t)kLdsBudget) {
+      hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(waves * kWave),
+                         lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
+                         per_rank, per_node_e, lay.expert_count,
+                         lay.expert_off, lay.rank_count, lay.rank_off,
+                         lay.rank_token_count, lay.node_mask, lay.node_count,
+                         lay.node_off, lay.node_slot, lay.slot_pos,
+                         lay.row_src, err);
+      return hipGetLastError();
+    }
+  }
   if (g.nblocks > 0) {
     const size_t lds = (size_t)g.tile_waves * g.cols * 8;
     hipLaunchKernelGGL(layout_count_kernel, dim3(g.nblocks), dim3(threads),
