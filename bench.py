@@ -229,6 +229,8 @@ def main() -> int:
     ap.add_argument("--gamma", type=float, default=1.25,
                     help="capacity factor of --path capacity")
     ap.add_argument("--part-dtype", default="bf16", choices=("bf16", "f32"))
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time replays")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-step distribution, cold-cache steps "
                          "and the copy ceiling")
@@ -289,14 +291,35 @@ def main() -> int:
                         stream)
 
     def step():
+        # current stream: the launch stream, or the capture stream of --graph
         moe.moe_dispatch_combine(cfg, x, lg, scale, idx, wt, lay, send, out,
-                                 ws, stream)
+                                 ws)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if moe.moe_read_device_error(ws) != 0:
         raise RuntimeError("device reported an input error")
+    eager_step = step
+    if args.graph:
+        # the library enqueues kernel launches only, so a step captures
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+        torch.cuda.synchronize()
+
+        def step():
+            graph.replay()
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
 
     # ---- timed region: exactly K fused steps --------------------------------
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -324,7 +347,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E,
                    "K": w.K, "R": w.R, "N": w.N, "rows": w.x_dtype,
-                   "accumulate": "f32", "seed": w.seed},
+                   "accumulate": "f32", "seed": w.seed,
+                   "launch": "hip-graph" if args.graph else "stream"},
         "hbm": {"alg_bytes": alg, "gbps": gbps,
                 "frac_of_peak": gbps / HBM_PEAK_GBPS},
     }

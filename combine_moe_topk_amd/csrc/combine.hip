@@ -61,8 +61,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
   }
   char *orow = out + (size_t)t * obytes;
+  // blockIdx.y picks the part of the row when a row is split over blocks
+  const int chunk = (U + gridDim.y - 1) / gridDim.y;
+  const int lo = blockIdx.y * chunk;
+  const int hi = min(U, lo + chunk);
 
-  for (int base = 0; base < U; base += TPT * UPT) {
+  for (int base = lo; base < hi; base += TPT * UPT) {
     float acc[UPT][8];
 #pragma unroll
     for (int j = 0; j < UPT; ++j)
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
         const char *row = y + (size_t)s * ybytes;
 #pragma unroll
         for (int j = 0; j < UPT; ++j)
-          u[k][j].load(row, min(base + j * TPT + tt, U - 1));
+          u[k][j].load(row, min(base + j * TPT + tt, hi - 1));
       }
 #pragma unroll
       for (int k = 0; k < KT; ++k) {
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
         Unit<YBF16> u[UPT];
 #pragma unroll
         for (int j = 0; j < UPT; ++j)
-          u[j].load(row, min(base + j * TPT + tt, U - 1));
+          u[j].load(row, min(base + j * TPT + tt, hi - 1));
 #pragma unroll
         for (int j = 0; j < UPT; ++j)
 #pragma unroll
@@ -109,7 +113,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
       const int i = base + j * TPT + tt;
-      if (i < U) store_unit<OBF16>(orow, i, acc[j]);
+      if (i < hi) store_unit<OBF16>(orow, i, acc[j]);
     }
   }
 }
@@ -123,17 +127,16 @@ constexpr int upt_for() {
   return raw < 1 ? 1 : (raw > 8 ? 8 : raw);
 }
 
-template <bool YB, bool OB, int KT, int TPT>
+template <bool YB, bool OB, int KT, int TPT, int UPT = upt_for<YB, KT>()>
 hipError_t launch_kt(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                      const float *w, const int32_t *idx, const float *scale,
-                     void *out, int rows, hipStream_t s) {
-  constexpr int UPT = upt_for<YB, KT>();
+                     void *out, int rows, int parts, hipStream_t s) {
   constexpr int kTokensPerBlock = 256 / TPT;
   const int U = c.H / 8;
-  const int grid = (c.T + kTokensPerBlock - 1) / kTokensPerBlock;
-  hipLaunchKernelGGL((combine_kernel<YB, OB, KT, UPT, TPT>), dim3(grid),
-                     dim3(256), 0, s, (const char *)y, slot_pos, w, idx,
-                     scale, (char *)out, c.T, c.K, U, rows);
+  const dim3 grid((c.T + kTokensPerBlock - 1) / kTokensPerBlock, parts);
+  hipLaunchKernelGGL((combine_kernel<YB, OB, KT, UPT, TPT>), grid, dim3(256),
+                     0, s, (const char *)y, slot_pos, w, idx, scale,
+                     (char *)out, c.T, c.K, U, rows);
   return hipGetLastError();
 }
 
@@ -141,10 +144,16 @@ template <bool YB, bool OB, int KT>
 hipError_t launch_k(const moe_cfg &c, const void *y, const int32_t *slot_pos,
                     const float *w, const int32_t *idx, const float *scale,
                     void *out, int rows, hipStream_t s) {
+  const int U = c.H / 8;
+  // Few tokens: one unit per thread, a wave per token and the row split in
+  // 64-unit parts over blockIdx.y, so the grid still fills the CUs.
+  if (c.T < 1024 && U > 64)
+    return launch_kt<YB, OB, KT, 64, 1>(c, y, slot_pos, w, idx, scale, out,
+                                        rows, (U + 63) / 64, s);
   // one wave per token while 64*UPT units cover the row, else a workgroup
-  if (c.H / 8 <= 64 * upt_for<YB, KT>())
-    return launch_kt<YB, OB, KT, 64>(c, y, slot_pos, w, idx, scale, out, rows, s);
-  return launch_kt<YB, OB, KT, 256>(c, y, slot_pos, w, idx, scale, out, rows, s);
+  if (U <= 64 * upt_for<YB, KT>())
+    return launch_kt<YB, OB, KT, 64>(c, y, slot_pos, w, idx, scale, out, rows, 1, s);
+  return launch_kt<YB, OB, KT, 256>(c, y, slot_pos, w, idx, scale, out, rows, 1, s);
 }
 
 template <bool YB, bool OB>

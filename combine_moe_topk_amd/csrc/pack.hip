@@ -31,12 +31,16 @@ __global__ __launch_bounds__(256) void pack_kernel(
   if (t >= T) return;  // one token per wave: uniform exit
   const int my_slot = lane < W ? slot_pos[(size_t)t * W + lane] : -1;
   const u32x4 *src = x + (size_t)t * V;
-  for (int base = 0; base < V; base += kWave * VPL) {
+  // blockIdx.y picks the part of the row when a row is split over waves
+  const int chunk = (V + gridDim.y - 1) / gridDim.y;
+  const int lo = blockIdx.y * chunk;
+  const int hi = min(V, lo + chunk);
+  for (int base = lo; base < hi; base += kWave * VPL) {
     u32x4 v[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int i = base + j * kWave + lane;
-      if (i < V) v[j] = src[i];
+      if (i < hi) v[j] = src[i];
     }
     for (int k = 0; k < W; ++k) {
       const int s = __builtin_amdgcn_readlane(my_slot, k);
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(256) void pack_kernel(
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         const int i = base + j * kWave + lane;
-        if (i < V) dst[i] = v[j];
+        if (i < hi) dst[i] = v[j];
       }
     }
   }
@@ -53,9 +57,9 @@ __global__ __launch_bounds__(256) void pack_kernel(
 
 template <int VPL>
 hipError_t launch_vpl(const void *x, const int32_t *slots, void *dst, int T,
-                      int W, int V, int rows, hipStream_t s) {
-  const int grid = (T + 3) / 4;
-  hipLaunchKernelGGL((pack_kernel<VPL>), dim3(grid), dim3(256), 0, s,
+                      int W, int V, int rows, int parts, hipStream_t s) {
+  const dim3 grid((T + 3) / 4, parts);
+  hipLaunchKernelGGL((pack_kernel<VPL>), grid, dim3(256), 0, s,
                      (const u32x4 *)x, slots, (u32x4 *)dst, T, W, V, rows);
   return hipGetLastError();
 }
@@ -68,11 +72,15 @@ hipError_t launch_pack_rows(const void *x, const int32_t *slots, int W,
   if (T == 0) return hipSuccess;
   const int V = row_bytes / 16;  // 16-byte vectors per row
   const int need = (V + kWave - 1) / kWave;
-  if (need <= 1) return launch_vpl<1>(x, slots, dst, T, W, V, rows, stream);
-  if (need <= 2) return launch_vpl<2>(x, slots, dst, T, W, V, rows, stream);
-  if (need <= 4) return launch_vpl<4>(x, slots, dst, T, W, V, rows, stream);
-  if (need <= 8) return launch_vpl<8>(x, slots, dst, T, W, V, rows, stream);
-  return launch_vpl<16>(x, slots, dst, T, W, V, rows, stream);
+  // Few tokens (fewer than 2048 waves at one wave a token): one wave per
+  // (token, 1 KiB piece of the row) instead, so the grid still fills the CUs.
+  if (T < 2048 && need > 1)
+    return launch_vpl<1>(x, slots, dst, T, W, V, rows, need, stream);
+  if (need <= 1) return launch_vpl<1>(x, slots, dst, T, W, V, rows, 1, stream);
+  if (need <= 2) return launch_vpl<2>(x, slots, dst, T, W, V, rows, 1, stream);
+  if (need <= 4) return launch_vpl<4>(x, slots, dst, T, W, V, rows, 1, stream);
+  if (need <= 8) return launch_vpl<8>(x, slots, dst, T, W, V, rows, 1, stream);
+  return launch_vpl<16>(x, slots, dst, T, W, V, rows, 1, stream);
 }
 
 hipError_t launch_pack(const moe_cfg &c, const void *x,
