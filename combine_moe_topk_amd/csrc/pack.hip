@@ -5,18 +5,29 @@
 // destination, before they are sent; on one GPU the destination chunks are
 // the expert-major segments of `send`.
 //
-// HBM-bound copy: each x row is read once into registers (16-byte vectors,
-// one wave per token, lanes striding the row so every load instruction moves
-// 1 KiB contiguously) and stored K times with ordinary 16-byte stores.  The K
-// destination rows are wave-uniform: lane k loads slot_pos[t,k] and the wave
-// reads it back with readlane, so the store addresses come from SGPRs.  The
-// same kernel serves any table of W <= 64 destination rows per token (K for
+// HBM-bound copy.  Main kernel: one wave per (token, piece of 128 16-byte
+// vectors, pair of destinations), pairs fastest, so the W/2 waves that copy
+// one piece of a row run side by side: the first one's load brings the
+// piece into the cache and the others hit it, so x still crosses HBM about
+// once.  Each wave loads its 2 KiB piece once and stores it to its two
+// destination rows (wave-uniform: scalar loads of slots[t,k]); every load or
+// store instruction moves 1 KiB contiguously, and stores are non-temporal:
+// the rows of `send` are not read again by this kernel.
+// Measured on MI355X with the combine running between packs (as in a real
+// step): 358 us for the DeepSeek-V3 shape (K = 8) and 1505 us for the Kimi
+// K2 shape (K = 16), against 388 and 1536 us for the kernel below, which
+// reads a whole row once into registers and stores it W times with ordinary
+// stores.  One destination per wave was as fast at K = 8 but 20% slower at
+// K = 16; ordinary stores cost 17% at K = 8.  For destination tables of
+// less than 1 GiB (Qwen3, Mixtral, decode shapes) the row kernel was the
+// faster one (49 against 55 us at Qwen3's shape, 8.0 against 10.3 us for
+// 128-token decode) and the combine after it ran faster too: its ordinary
+// stores leave part of `send` in the 256 MB last-level cache.  So the piece
+// kernel runs from 1 GiB of destination rows up (and below 2^31 waves of
+// work), the row kernel otherwise.
+// Both kernels serve any table of W <= 64 destination rows per token (K for
 // the expert-major pack, N for the node-level pack); entries outside
 // [0, rows) are skipped.
-// Measured on MI355X with the combine running between packs (as in a real
-// step): ordinary stores, which the last-level cache can merge before they
-// reach HBM, beat non-temporal stores by ~11% (392 vs 441 us for the
-// DeepSeek-V3 shape), and reach the chip's plain copy rate (~5.4 TB/s).
 #include "moe_internal.h"
 
 namespace moe {
@@ -55,6 +66,40 @@ __global__ __launch_bounds__(256) void pack_kernel(
   }
 }
 
+constexpr int kPieceVP = 2;  // 16-byte vectors per lane in a piece
+constexpr int kPieceG = 2;   // destinations per wave
+constexpr size_t kPieceMinBytes = size_t(1) << 30;  // destination rows
+
+__global__ __launch_bounds__(256) void pack_piece_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ slots,
+    u32x4 *__restrict__ send, int W, int V, int P, int NG, int rows, int n) {
+  const int lane = threadIdx.x % kWave;
+  // wave index made wave-uniform so the index arithmetic runs on the SALU
+  const int g = blockIdx.x * (256 / kWave) +
+                __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (g >= n) return;  // n = T*P*NG waves of work
+  const int q = g % NG;  // NG = ceil(W / kPieceG) destination groups
+  const int p = (g / NG) % P;
+  const int t = g / (NG * P);
+  const int base = p * kPieceVP * kWave + lane;
+  const u32x4 *src = x + (size_t)t * V;
+  u32x4 v[kPieceVP];  // clamped loads: no branch, all in flight together
+#pragma unroll
+  for (int j = 0; j < kPieceVP; ++j) v[j] = src[min(base + j * kWave, V - 1)];
+#pragma unroll
+  for (int d = 0; d < kPieceG; ++d) {
+    const int k = q * kPieceG + d;
+    if (k >= W) break;
+    const int s = slots[(size_t)t * W + k];
+    if ((unsigned)s >= (unsigned)rows) continue;  // out-of-range: skipped
+    u32x4 *dst = send + (size_t)s * V;
+#pragma unroll
+    for (int j = 0; j < kPieceVP; ++j)
+      if (base + j * kWave < V)
+        __builtin_nontemporal_store(v[j], dst + base + j * kWave);
+  }
+}
+
 template <int VPL>
 hipError_t launch_vpl(const void *x, const int32_t *slots, void *dst, int T,
                       int W, int V, int rows, int parts, hipStream_t s) {
@@ -71,6 +116,15 @@ hipError_t launch_pack_rows(const void *x, const int32_t *slots, int W,
                             hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int V = row_bytes / 16;  // 16-byte vectors per row
+  const int P = (V + kWave * kPieceVP - 1) / (kWave * kPieceVP);
+  const int NG = (W + kPieceG - 1) / kPieceG;
+  const long n = (long)T * P * NG;
+  if ((size_t)rows * row_bytes >= kPieceMinBytes && n <= 0x7fffffffL) {
+    hipLaunchKernelGGL(pack_piece_kernel, dim3((unsigned)((n + 3) / 4)),
+                       dim3(256), 0, stream, (const u32x4 *)x, slots,
+                       (u32x4 *)dst, W, V, P, NG, rows, (int)n);
+    return hipGetLastError();
+  }
   const int need = (V + kWave - 1) / kWave;
   // Few tokens (fewer than 2048 waves at one wave a token): one wave per
   // (token, 1 KiB piece of the row) instead, so the grid still fills the CUs.

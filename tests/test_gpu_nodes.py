@@ -126,6 +126,26 @@ def test_pack_nodes(w):
     assert not got[len(ref):].any()  # rows past the crossings untouched
 
 
+def test_pack_nodes_large_ragged():
+    # 200000 node rows of 6000 bytes: the pack's piece-per-wave kernel, with
+    # a ragged last piece per row, an odd node count and skipped (-1) entries
+    w = mi.Workload("large_ragged", T=40000, H=3000, E=60, K=5, R=15, N=5,
+                    x_dtype=mi.BF16, out_dtype=mi.BF16)
+    cfg = cfg_of(w)
+    cap = moe.moe_node_rows_max(cfg)
+    assert cap * w.H * 2 >= 1 << 30
+    x = mi.random_x(w.T, w.H, w.x_dtype, seed=4)
+    idx = mi.random_topk_idx(w.T, w.E, w.K, seed=4)
+    lay = oracle.layout(idx, w.E, w.R, w.N)
+    assert (lay["node_slot"] < 0).any()
+    ns = torch.zeros((cap, w.H), dtype=row_dtype(w), device="cuda")
+    moe.moe_dispatch_pack_nodes(cfg, dev(x), dev(lay["node_slot"]), ns)
+    ref = oracle.pack_nodes(x, lay["node_slot"])
+    got = host(ns)
+    np.testing.assert_array_equal(got[:len(ref)], ref)
+    assert not got[len(ref):].any()
+
+
 @pytest.mark.parametrize("w", SMALL, ids=_ids)
 def test_forward(w):
     d = mi.make_inputs(w)

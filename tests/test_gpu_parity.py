@@ -163,6 +163,24 @@ def test_pack(w):
     np.testing.assert_array_equal(host(send), ref_send)
 
 
+# The pack switches to its piece-per-wave kernel from 1 GiB of destination
+# rows up: this shape (200000 rows of 6000 bytes) reaches it with a ragged
+# last piece per row (375 16-byte vectors, pieces of 128) and an odd K.
+LARGE_RAGGED = mi.Workload("large_ragged", T=40000, H=3000, E=60, K=5, R=15,
+                           N=5, x_dtype=mi.BF16, out_dtype=mi.BF16)
+
+
+def test_pack_large_ragged():
+    w = LARGE_RAGGED
+    assert w.T * w.K * w.H * 2 >= 1 << 30
+    x = mi.random_x(w.T, w.H, w.x_dtype, seed=3)
+    idx = mi.random_topk_idx(w.T, w.E, w.K, seed=3)
+    slot_pos = oracle.layout(idx, w.E, w.R, w.N)["slot_pos"]
+    send = torch.zeros((w.T * w.K, w.H), dtype=row_dtype(w), device="cuda")
+    moe.moe_dispatch_pack(cfg_of(w), dev(x), dev(slot_pos), send)
+    np.testing.assert_array_equal(host(send), oracle.pack(x, slot_pos))
+
+
 # -------------------------------------------------------------- combine ----
 
 @pytest.mark.parametrize("ydt,odt", [(mi.BF16, mi.BF16), (mi.F32, mi.F32),
