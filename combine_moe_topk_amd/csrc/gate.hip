@@ -178,11 +178,13 @@ __global__ __launch_bounds__(256) void gate_kernel(
   if (!live) t = T - 1;
   const float *row = logits + (size_t)t * E;
 
+  // clamped loads (no branch): all C are in flight before the first use
   uint32_t key[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int e = sub + j * G;
-    key[j] = e < E ? order_bits(row[e]) : 0u;
+    const float v = row[min(e, E - 1)];
+    key[j] = e < E ? order_bits(v) : 0u;
   }
   Cache cache;
   cache.lk = 0u;
@@ -216,7 +218,11 @@ __global__ __launch_bounds__(256) void gate_kernel(
   if (renorm) {
     denom = ex;
   } else {
-    for (int e = sub; e < E; e += G) denom += exp((double)row[e] - mx);
+    // every logit of the lane is in its keys (C*G >= E); -0.0 came back
+    // as +0.0, which gives the same exp(l - max)
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      if (sub + j * G < E) denom += exp((double)from_order_bits(key[j]) - mx);
   }
   denom = group_sum_f64<G>(denom);
 

@@ -37,6 +37,18 @@ __device__ __forceinline__ void raise_error(int32_t *err, int bits) {
   if (bits) atomicOr(err, bits);
 }
 
+// A token's K expert ids into registers, KM >= K of them: the index of every
+// load is clamped into the row, so the loads have no branches and all go out
+// before the first use (a guarded or data-dependent loop would wait for
+// each load in turn: K memory round trips instead of one).
+template <int KM>
+__device__ __forceinline__ void load_ids(const int32_t *row, int K,
+                                         int (&ev)[KM]) {
+#pragma unroll
+  for (int k = 0; k < KM; ++k) ev[k] = row[min(k, K - 1)];
+}
+
+template <int KM>
 __global__ __launch_bounds__(1024) void layout_count_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
     int per_rank, int per_node_e, uint64_t *__restrict__ node_mask,
@@ -46,18 +58,21 @@ __global__ __launch_bounds__(1024) void layout_count_kernel(
   const int W = blockDim.x / kWave;
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  int ev[KM];
+  if (t < T) load_ids<KM>(idx + (size_t)t * K, K, ev);
   for (int i = threadIdx.x; i < W * cols; i += blockDim.x) bm[i] = 0;
   __syncthreads();
 
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t bit = 1ull << lane;
   uint64_t *mine = bm + (size_t)w * cols;
   int bad = 0;
   if (t < T) {
     uint64_t mask = 0;
-    const int32_t *row = idx + (size_t)t * K;
-    for (int k = 0; k < K; ++k) {
-      const int e = row[k];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k >= K) break;
+      const int e = ev[k];
       if ((unsigned)e >= (unsigned)E) {
         bad |= MOE_DEVERR_EXPERT_RANGE;
         continue;
@@ -182,6 +197,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
   }
 }
 
+template <int KM>
 __global__ __launch_bounds__(1024) void layout_rank_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
     int per_node_e, const int32_t *__restrict__ table,
@@ -193,6 +209,9 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   const int W = blockDim.x / kWave;
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  int ev[KM];
+  if (t < T) load_ids<KM>(idx + (size_t)t * K, K, ev);
   uint64_t *bm = sm;                                  // [W][cr]
   int32_t *base = (int32_t *)(sm + (size_t)W * cr);   // [cr]
   for (int i = threadIdx.x; i < W * cr; i += blockDim.x) bm[i] = 0;
@@ -204,15 +223,15 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
       base[E + n] = tail[E + R + n] + tile[E + R + n];
   __syncthreads();
 
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const uint64_t bit = 1ull << lane;
   const uint64_t below = bit - 1;
   uint64_t *mine = bm + (size_t)w * cr;
   uint64_t mask = 0;
   if (t < T) {
-    const int32_t *row = idx + (size_t)t * K;
-    for (int k = 0; k < K; ++k) {
-      const int e = row[k];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k >= K) break;
+      const int e = ev[k];
       if ((unsigned)e >= (unsigned)E) continue;
       atomicOr((unsigned long long *)&mine[e], bit);
       mask |= 1ull << (e / per_node_e);
@@ -225,10 +244,11 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   __syncthreads();
   if (t >= T) return;
 
-  const int32_t *row = idx + (size_t)t * K;
-  for (int k = 0; k < K; ++k) {
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    if (k >= K) break;
     const size_t i = (size_t)t * K + k;
-    const int e = row[k];
+    const int e = ev[k];
     if ((unsigned)e >= (unsigned)E) {
       slot_pos[i] = -1;
       continue;
@@ -253,6 +273,7 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
 // The whole layout in one workgroup when every token fits in one tile (the
 // decode case): the same LDS bitmaps give the counts, the offsets (scanned in
 // LDS) and the ranks, in one launch instead of three.
+template <int KM>
 __global__ __launch_bounds__(1024) void layout_single_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
     int per_rank, int per_node_e, int32_t *__restrict__ expert_count,
@@ -270,19 +291,22 @@ __global__ __launch_bounds__(1024) void layout_single_kernel(
   int32_t *tot = (int32_t *)(bm + (size_t)W * cols);  // [cols]
   int32_t *eoff = tot + cols;                          // [E + 1]
   int32_t *noff = eoff + E + 1;                        // [N + 1]
+  const int t = threadIdx.x;
+  int ev[KM];
+  if (t < T) load_ids<KM>(idx + (size_t)t * K, K, ev);
   for (int i = threadIdx.x; i < W * cols; i += blockDim.x) bm[i] = 0;
   __syncthreads();
 
-  const int t = threadIdx.x;
   const uint64_t bit = 1ull << lane;
   const uint64_t below = bit - 1;
   uint64_t *mine = bm + (size_t)w * cols;
   uint64_t mask = 0;
   int bad = 0;
   if (t < T) {
-    const int32_t *row = idx + (size_t)t * K;
-    for (int k = 0; k < K; ++k) {
-      const int e = row[k];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k >= K) break;
+      const int e = ev[k];
       if ((unsigned)e >= (unsigned)E) {
         bad |= MOE_DEVERR_EXPERT_RANGE;
         continue;
@@ -332,10 +356,11 @@ __global__ __launch_bounds__(1024) void layout_single_kernel(
   __syncthreads();
 
   if (t >= T) return;
-  const int32_t *row = idx + (size_t)t * K;
-  for (int k = 0; k < K; ++k) {
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    if (k >= K) break;
     const size_t i = (size_t)t * K + k;
-    const int e = row[k];
+    const int e = ev[k];
     if ((unsigned)e >= (unsigned)E) {
       slot_pos[i] = -1;
       continue;
@@ -379,9 +404,12 @@ LayoutGeom layout_geom(const moe_cfg &c) {
   return g;
 }
 
-hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
-                         const moe_layout &lay, void *ws,
-                         hipStream_t stream) {
+namespace {
+
+template <int KM>
+hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
+                            const moe_layout &lay, void *ws,
+                            hipStream_t stream) {
   const LayoutGeom g = layout_geom(c);
   int32_t *err = (int32_t *)ws;
   int32_t *table = (int32_t *)((char *)ws + kWsHeader);
@@ -395,7 +423,7 @@ hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
     const size_t lds = (size_t)waves * g.cols * 8 +
                        (size_t)(g.cols + c.E + 1 + c.N + 1) * 4;
     if (lds <= (size_t)kLdsBudget) {
-      hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(waves * kWave),
+      hipLaunchKernelGGL(layout_single_kernel<KM>, dim3(1), dim3(waves * kWave),
                          lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
                          per_rank, per_node_e, lay.expert_count,
                          lay.expert_off, lay.rank_count, lay.rank_off,
@@ -407,7 +435,7 @@ hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
   }
   if (g.nblocks > 0) {
     const size_t lds = (size_t)g.tile_waves * g.cols * 8;
-    hipLaunchKernelGGL(layout_count_kernel, dim3(g.nblocks), dim3(threads),
+    hipLaunchKernelGGL(layout_count_kernel<KM>, dim3(g.nblocks), dim3(threads),
                        lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
                        per_rank, per_node_e, lay.node_mask, table, err);
     hipError_t e = hipGetLastError();
@@ -428,7 +456,7 @@ hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
   if (g.nblocks > 0) {
     const size_t lds = (size_t)g.tile_waves * (c.E + c.N) * 8 +
                        (size_t)(c.E + c.N) * 4;
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.nblocks), dim3(threads),
+    hipLaunchKernelGGL(layout_rank_kernel<KM>, dim3(g.nblocks), dim3(threads),
                        lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
                        per_node_e, table, lay.slot_pos,
                        lay.row_src, lay.node_slot);
@@ -436,6 +464,17 @@ hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
+                         const moe_layout &lay, void *ws,
+                         hipStream_t stream) {
+  if (c.K <= 4) return launch_layout_km<4>(c, topk_idx, lay, ws, stream);
+  if (c.K <= 8) return launch_layout_km<8>(c, topk_idx, lay, ws, stream);
+  if (c.K <= 16) return launch_layout_km<16>(c, topk_idx, lay, ws, stream);
+  return launch_layout_km<32>(c, topk_idx, lay, ws, stream);  // K <= 32
 }
 
 }  // namespace moe
