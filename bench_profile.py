@@ -3,8 +3,12 @@
   python bench_profile.py trace  <results.db> <out.md> --cmd "<command>"
   python bench_profile.py traffic <fetch.db> <write.db> --workload NAME \
         --calib-mib MIB --cmd-fetch "<command>" --cmd-write "<command>"
+  python bench_profile.py lds <results.db> <out.md> --cmd "<command>"
 
 `trace` writes per-kernel duration statistics from a --kernel-trace run.
+`lds` summarises a run with SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE and
+SQ_INSTS_LDS: per kernel, the cycles LDS spent on bank conflicts against the
+cycles it was busy with indexed accesses.
 `traffic` reads a FETCH_SIZE run and a WRITE_SIZE run of
 `bench.py --fused-only ... --copy-calib-mib MIB`, scales each counter by what
 it reads for the calibration copy (a device copy of MIB MiB, which reads and
@@ -112,6 +116,35 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
         f.write("\n".join(md))
 
 
+def lds(db: str, out: str, cmd: str) -> None:
+    c = sqlite3.connect(db)
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for n, counter, v in c.execute(
+            "select kernel_name, counter_name, value from counters_collection"):
+        per[short(n)][counter].append(v)
+    lines = ["# LDS bank conflicts per dispatch\n", "Command:\n",
+             f"    {cmd}\n",
+             "Counters averaged over dispatches; conflict share = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles).\n", "```",
+             f"{'kernel':44s} {'n':>4s} {'LDS instrs':>11s} {'active cyc':>11s} "
+             f"{'conflict cyc':>12s} {'share':>6s}"]
+    rows = []
+    for k, d in per.items():
+        ins = d.get("SQ_INSTS_LDS", [0])
+        act = d.get("SQ_LDS_IDX_ACTIVE", [0])
+        con = d.get("SQ_LDS_BANK_CONFLICT", [0])
+        a, b = sum(act) / len(act), sum(con) / len(con)
+        if sum(ins) == 0:
+            continue
+        rows.append((k, len(ins), sum(ins) / len(ins), a, b,
+                     b / a if a else float("nan")))
+    for k, n, i, a, b, r in sorted(rows, key=lambda r: -r[3]):
+        lines.append(f"{k:44s} {n:4d} {i:11.0f} {a:11.0f} {b:12.0f} {r:6.3f}")
+    lines.append("```\n")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -119,6 +152,10 @@ def main() -> None:
     t.add_argument("db")
     t.add_argument("out")
     t.add_argument("--cmd", required=True)
+    l = sub.add_parser("lds")
+    l.add_argument("db")
+    l.add_argument("out")
+    l.add_argument("--cmd", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("fetch_db")
     r.add_argument("write_db")
@@ -129,6 +166,8 @@ def main() -> None:
     a = ap.parse_args()
     if a.what == "trace":
         trace(a.db, a.out, a.cmd)
+    elif a.what == "lds":
+        lds(a.db, a.out, a.cmd)
     else:
         traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
                 a.cmd_write)
