@@ -118,8 +118,15 @@ def cpu_baseline(w: mi.Workload, d: dict, sample_tokens: int) -> dict:
     oracle.dispatch_combine(x, lg, w.K, w.R, w.N, d["expert_scale"],
                             w.out_dtype)
     dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f
+                        if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": Ts / dt, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu, "host_cpus": os.cpu_count(),
             "sample": f"first {Ts} of {w.T} tokens of {w.name}, whole path "
                       f"(gate, layout, pack, combine), one thread, "
                       f"{dt:.2f} s"}
