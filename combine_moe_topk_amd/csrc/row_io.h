@@ -42,6 +42,23 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// 8 fp32 values rounded into out's unit layout: one 16-byte vector of bf16
+// (v[0]) or two of fp32 (v[0], v[1]).
+template <bool OBF16>
+__device__ __forceinline__ void pack_unit(const float *a, u32x4 *v) {
+  if constexpr (OBF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[0][j] = bf16_rne(a[2 * j]) | (bf16_rne(a[2 * j + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[0][j] = __float_as_uint(a[j]);
+      v[1][j] = __float_as_uint(a[4 + j]);
+    }
+  }
+}
+
 template <bool OBF16>
 __device__ __forceinline__ void store_unit(char *row, int i, const float *a) {
   if constexpr (OBF16) {

@@ -208,6 +208,49 @@ def test_combine(w, ydt, odt):
         assert np.mean(got == ref_out) > 0.99
 
 
+# From 1 GiB of y rows the combine switches to its burst kernel (groups of 8
+# tokens reduced into LDS, then written together): this shape reaches it
+# with a ragged last group (45003 tokens), a row of 375 units (not a wave
+# multiple) and dropped slots (-1) that must add nothing.
+@pytest.mark.parametrize("odt", [mi.BF16, mi.F32])
+def test_combine_burst_ragged(odt):
+    w = mi.Workload("burst_ragged", T=45003, H=3000, E=60, K=4, R=15, N=5,
+                    x_dtype=mi.BF16, out_dtype=odt)
+    assert w.T * w.K * w.H * 2 >= 1 << 30 and w.T % 8 == 3
+    idx = mi.random_topk_idx(w.T, w.E, w.K, seed=5)
+    rng = np.random.Generator(np.random.PCG64(5))
+    # weights summing to 1, as the gate gives: |out| stays below 8, where
+    # the bf16 rounding step is within the 2e-2 bound
+    wt = rng.random((w.T, w.K), dtype=np.float32) + np.float32(0.1)
+    wt = (wt / wt.sum(axis=1, keepdims=True)).astype(np.float32)
+    scale = (1.0 + 0.01 * (np.arange(w.E) % 8)).astype(np.float32)
+    slot_pos = oracle.layout(idx, w.E, w.R, w.N)["slot_pos"].copy()
+    drop = rng.random((w.T, w.K)) < 0.05
+    drop[-1, :] = True  # the last token: every slot dropped, so out is 0
+    slot_pos[drop] = -1
+    # 1 GiB of rows drawn from 4096 distinct seeded rows (cheap to generate)
+    y = mi.random_x(4096, w.H, mi.BF16, seed=6)[
+        rng.integers(0, 4096, w.T * w.K)]
+    out = torch.empty((w.T, w.H), dtype=out_dtype(w), device="cuda")
+    moe.moe_combine(cfg_of(w), dev(y), dev(slot_pos), dev(wt), dev(idx),
+                    dev(scale), out)
+    got = host(out)
+    ref_out, exact = oracle.combine(y, slot_pos, wt, idx, scale, odt)
+    if odt == mi.BF16:
+        check_out(got, exact, None, odt)
+        assert np.mean(got == ref_out) > 0.99
+    else:
+        toks = np.unique(np.concatenate(
+            [np.arange(16), np.arange(w.T - 3, w.T),
+             rng.integers(0, w.T, 256)]))
+        coef = np.where(drop, 0.0, wt.astype(np.float64) * scale[idx])
+        sp = np.where(drop, 0, slot_pos)[toks]
+        ysel = rows_f64(y[sp.ravel()]).reshape(len(toks), w.K, w.H)
+        bound = np.einsum("tk,tkh->th", np.abs(coef[toks]), np.abs(ysel))
+        check_out(got[toks], exact[toks], bound, odt)
+    assert not got[-1].any()
+
+
 # ---------------------------------------------------------------- fused ----
 
 @pytest.mark.parametrize("w", SMALL, ids=_ids)
