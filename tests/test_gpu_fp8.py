@@ -6,6 +6,8 @@ combine of FP8 rows is held to the combine tolerances (fp32 outputs within
 1e-5 of sum|terms|, bf16 outputs within 2e-2 absolute of the oracle's
 unrounded fp64 sum of the dequantised rows).
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -153,6 +155,43 @@ def test_combine_fp8(w):
     _check_out(host(out), exact,
                _term_scale(_deq_rows(send, w.H, B), lay["slot_pos"],
                            _coef(d, idx, wt)), w.out_dtype)
+
+
+# From 512 MiB of FP8 rows the combine switches to its burst kernel (groups
+# of 8 tokens staged in LDS): 20001 tokens leave a ragged last group.
+@functools.lru_cache(maxsize=1)
+def _burst_case():
+    w = mi.Workload("fp8_burst_ragged", T=20001, H=4096, E=64, K=8, R=16,
+                    N=4, x_dtype=mi.BF16)
+    B = 128
+    d = mi.make_inputs(w)
+    idx, wt = oracle.gate(d["logits"], w.K)
+    lay = oracle.layout(idx, w.E, w.R, w.N)
+    send = oracle.pack_fp8(d["x"], lay["slot_pos"], B)
+    _, exact = oracle.combine_fp8(send, lay["slot_pos"], wt, w.H, B, idx,
+                                  d["expert_scale"], "f32")
+    return w, B, d, idx, wt, lay, send, exact
+
+
+@pytest.mark.parametrize("odt", [mi.BF16, mi.F32])
+def test_combine_fp8_burst_ragged(odt):
+    w, B, d, idx, wt, lay, send, exact = _burst_case()
+    w = w.replace(out_dtype=odt)
+    assert w.T * w.K * moe.moe_fp8_row_bytes(w.H, B) >= 512 << 20
+    out = torch.empty((w.T, w.H), dtype=out_dtype(w), device="cuda")
+    moe.moe_combine_fp8(cfg_of(w), dev(send), dev(lay["slot_pos"]), dev(wt),
+                        dev(idx), dev(d["expert_scale"]), out, B)
+    got = host(out)
+    rng = np.random.Generator(np.random.PCG64(3))
+    toks = np.unique(np.concatenate([np.arange(16), np.arange(w.T - 3, w.T),
+                                     rng.integers(0, w.T, 256)]))
+    sp = lay["slot_pos"][toks]
+    deq = _deq_rows(send[sp.ravel()], w.H, B).reshape(len(toks), w.K, w.H)
+    coef = _coef(d, idx, wt)[toks]
+    bound = np.einsum("tk,tkh->th", np.abs(coef), np.abs(deq))
+    _check_out(got[toks], exact[toks], bound, odt)
+    if odt == mi.BF16:
+        _check_out(got, exact, None, odt)  # every token, absolute bound
 
 
 # ------------------------------------------------------ fused path ----
