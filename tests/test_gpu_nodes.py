@@ -162,6 +162,27 @@ def test_forward(w):
                                   oracle.pack(d["x"], lay["slot_pos"]))
 
 
+def test_forward_large_ragged():
+    # 1.2 GB of send rows with a row of 375 16-byte vectors (not a multiple
+    # of the wave's 64-vector stride), an odd K and 5 nodes
+    w = mi.Workload("large_ragged", T=40000, H=3000, E=60, K=5, R=15, N=5,
+                    x_dtype=mi.BF16, out_dtype=mi.BF16)
+    assert w.T * w.K * w.H * 2 >= 1 << 30
+    cfg = cfg_of(w)
+    x = mi.random_x(w.T, w.H, w.x_dtype, seed=8)
+    idx = mi.random_topk_idx(w.T, w.E, w.K, seed=8)
+    lay = oracle.layout(idx, w.E, w.R, w.N)
+    ref_ns = oracle.pack_nodes(x, lay["node_slot"])
+    ns = torch.zeros((moe.moe_node_rows_max(cfg), w.H), dtype=row_dtype(w),
+                     device="cuda")
+    ns[:len(ref_ns)] = dev(ref_ns)
+    del ref_ns
+    send = torch.zeros((w.T * w.K, w.H), dtype=row_dtype(w), device="cuda")
+    moe.moe_dispatch_forward(cfg, ns, dev(lay["node_slot"]), dev(idx),
+                             dev(lay["slot_pos"]), send)
+    np.testing.assert_array_equal(host(send), oracle.pack(x, lay["slot_pos"]))
+
+
 @pytest.mark.parametrize("pdt", ["bf16", "f32"])
 @pytest.mark.parametrize("w", SMALL, ids=_ids)
 def test_partial(w, pdt):
