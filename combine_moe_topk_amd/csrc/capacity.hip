@@ -109,7 +109,10 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(
   if (r >= n || row_src[r] >= 0) return;  // uniform per wave
   const u32x4 z = {0u, 0u, 0u, 0u};
   u32x4 *row = rows + (size_t)r * V;
-  for (int i = lane; i < V; i += kWave) row[i] = z;
+  // non-temporal: ordinary stores leave up to 256 MB of dirty lines in the
+  // last-level cache, written back while the next step's pack runs (its
+  // time rose from ~360 to ~440 us for the DeepSeek-V3 shape)
+  for (int i = lane; i < V; i += kWave) __builtin_nontemporal_store(z, row + i);
 }
 
 }  // namespace

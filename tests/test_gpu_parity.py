@@ -328,6 +328,8 @@ def test_empty_input():
     (70, 1032, 8, 1, 8, 1, mi.F32, mi.F32),    # K = 1, 129 units
     (200, 136, 32, 5, 8, 4, mi.F32, mi.BF16),  # K not a power of two
     (129, 264, 64, 32, 64, 64, mi.BF16, mi.BF16),  # K = 32, N = 64
+    (300, 64, 4096, 8, 64, 8, mi.BF16, mi.BF16),  # E = 4096: 64-token tiles
+    (40, 16384, 16, 4, 4, 2, mi.BF16, mi.F32),  # H = 16384: 2048 units
 ])
 def test_fused_edge_shapes(T, H, E, K, R, N, xdt, odt):
     w = mi.Workload("edge", T=T, H=H, E=E, K=K, R=R, N=N, x_dtype=xdt,
