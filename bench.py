@@ -169,6 +169,20 @@ def extras(w, step, stream, alg, dev) -> dict:
         cold.append((a, b))
     torch.cuda.synchronize()
     cold = [a.elapsed_time(b) for a, b in cold]
+    # cold, clean: 1 GiB read between steps evicts the cache without leaving
+    # dirty lines (after the write flush above, their write-back to HBM runs
+    # inside the next step)
+    clean = []
+    for _ in range(n):
+        flush.sum(dtype=torch.int64)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        clean.append((a, b))
+    torch.cuda.synchronize()
+    clean = [a.elapsed_time(b) for a, b in clean]
     del flush
     # copy ceiling: 2 GiB device-to-device copies
     src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
@@ -209,6 +223,8 @@ def extras(w, step, stream, alg, dev) -> dict:
         "warm_ms": {"p10": _pct(warm, 10), "p50": med_w, "p90": _pct(warm, 90)},
         "cold_ms": {"p10": _pct(cold, 10), "p50": _pct(cold, 50),
                     "p90": _pct(cold, 90)},
+        "cold_clean_ms": {"p10": _pct(clean, 10), "p50": _pct(clean, 50),
+                          "p90": _pct(clean, 90)},
         "copy_ceiling_gbps": copy_gbps,
         "frac_of_copy_ceiling": alg / (med_w * 1e-3) / 1e9 / copy_gbps,
         "rocm": ver, "torch": torch.__version__,
