@@ -49,7 +49,10 @@ KERNEL_SOURCES = {
     "pack": ["combine_moe_topk_amd/csrc/pack.hip"],
     "combine": ["combine_moe_topk_amd/csrc/combine.hip",
                 "combine_moe_topk_amd/csrc/row_io.h"],
+    "assign": ["combine_moe_topk_amd/csrc/assign.hip"],
 }
+# int32 vector ALU issue rate: 256 CUs x 64 lanes x 2.4 GHz (lane-ops/s)
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 
 
 def kernel_bytes(w: mi.Workload) -> dict:
@@ -104,6 +107,19 @@ def load_traffic(kernel: str, workload: str):
     if ent.get("source_sha") != source_digest(KERNEL_SOURCES[kernel]):
         return None
     return ent.get("bytes_per_launch")
+
+
+def load_valu(workload: str):
+    """Vector instructions one moe_assign_tasks call issues, from committed
+    rocprofv3 counters; null when absent or the source changed since."""
+    p = os.path.join(ROOT, "profiles", "valu.json")
+    try:
+        ent = json.load(open(p))[f"assign/{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if ent.get("source_sha") != source_digest(KERNEL_SOURCES["assign"]):
+        return None
+    return ent.get("valu_insts_per_call")
 
 
 def cpu_baseline(w: mi.Workload, d: dict, sample_tokens: int) -> dict:
@@ -762,6 +778,11 @@ def assign_path(args, w, d, cfg, lg, idx, wt, stream) -> int:
           f"with replicas vs {without} without", file=sys.stderr, flush=True)
     T, K = w.T, w.K
     by = T * (4 * K + 8 * K + 4 + 4 * K + 8) + w.R * w.E + 8 * w.E
+    # issued vector instructions x 64 lanes (an upper bound on lane-ops:
+    # inactive lanes count) per second, against the int32 issue rate
+    valu_insts = load_valu(w.name)
+    achieved = (None if valu_insts is None
+                else valu_insts * 64 / (ms_assign * 1e-3) / 1e12)
     result = {
         "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -774,9 +795,13 @@ def assign_path(args, w, d, cfg, lg, idx, wt, stream) -> int:
         "crossings": {"with_replicas": with_rep, "home_only": without,
                       "ratio": with_rep / max(without, 1)},
         "roofline": {"kernel": "assign", "bound": "alu",
-                     "achieved": T / (ms_assign * 1e-3) / 1e6,
-                     "peak": None, "unit": "Mtokens/s", "frac": None,
+                     "achieved": achieved, "peak": ALU_PEAK_TOPS,
+                     "unit": "Tops/s",
+                     "frac": None if achieved is None
+                     else achieved / ALU_PEAK_TOPS,
                      "traffic": None, "alg_bytes_per_launch": by,
+                     "valu_insts_per_launch": valu_insts,
+                     "mtokens_per_s": T / (ms_assign * 1e-3) / 1e6,
                      "launch_ms": ms_assign},
     }
     print(json.dumps(result), flush=True)

@@ -4,11 +4,15 @@
   python bench_profile.py traffic <fetch.db> <write.db> --workload NAME \
         --calib-mib MIB --cmd-fetch "<command>" --cmd-write "<command>"
   python bench_profile.py lds <results.db> <out.md> --cmd "<command>"
+  python bench_profile.py valu <results.db> --workload NAME --cmd "<command>"
 
 `trace` writes per-kernel duration statistics from a --kernel-trace run.
 `lds` summarises a run with SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE and
 SQ_INSTS_LDS: per kernel, the cycles LDS spent on bank conflicts against the
 cycles it was busy with indexed accesses.
+`valu` reads a run of `bench.py --path assign` with SQ_INSTS_VALU and
+SQ_INSTS_SALU and records the vector instructions one moe_assign_tasks call
+issues (its two kernels) in profiles/valu.json, with the source hash.
 `traffic` reads a FETCH_SIZE run and a WRITE_SIZE run of
 `bench.py --fused-only ... --copy-calib-mib MIB`, scales each counter by what
 it reads for the calibration copy (a device copy of MIB MiB, which reads and
@@ -145,6 +149,35 @@ def lds(db: str, out: str, cmd: str) -> None:
         f.write("\n".join(lines))
 
 
+def valu(db: str, workload: str, cmd: str) -> None:
+    c = sqlite3.connect(db)
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for n, counter, v in c.execute(
+            "select kernel_name, counter_name, value from counters_collection"):
+        per[short(n)][counter].append(v)
+    parts = {k: {ctr: sum(v) / len(v) for ctr, v in d.items()}
+             for k, d in per.items()
+             if k.startswith(("assign_kernel", "expert_tables_kernel"))}
+    total = sum(d.get("SQ_INSTS_VALU", 0.0) for d in parts.values())
+    path = os.path.join(PROFILES, "valu.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[f"assign/{workload}"] = {
+        "valu_insts_per_call": total, "kernels": parts,
+        "source_sha": bench.source_digest(bench.KERNEL_SOURCES["assign"])}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    md = [f"# Vector instructions of moe_assign_tasks: {workload}\n",
+          "Command:\n", f"    {cmd}\n",
+          "Wave-level instruction counts per dispatch (averaged):\n", "```",
+          f"{'kernel':40s} {'SQ_INSTS_VALU':>14s} {'SQ_INSTS_SALU':>14s}"]
+    for k, d in sorted(parts.items()):
+        md.append(f"{k:40s} {d.get('SQ_INSTS_VALU', 0):14.0f} "
+                  f"{d.get('SQ_INSTS_SALU', 0):14.0f}")
+    md.append("```\n")
+    with open(os.path.join(PROFILES, f"valu_assign_{workload}.md"), "w") as f:
+        f.write("\n".join(md))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -156,6 +189,10 @@ def main() -> None:
     l.add_argument("db")
     l.add_argument("out")
     l.add_argument("--cmd", required=True)
+    v = sub.add_parser("valu")
+    v.add_argument("db")
+    v.add_argument("--workload", default="deepseek_v3")
+    v.add_argument("--cmd", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("fetch_db")
     r.add_argument("write_db")
@@ -168,6 +205,8 @@ def main() -> None:
         trace(a.db, a.out, a.cmd)
     elif a.what == "lds":
         lds(a.db, a.out, a.cmd)
+    elif a.what == "valu":
+        valu(a.db, a.workload, a.cmd)
     else:
         traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
                 a.cmd_write)
