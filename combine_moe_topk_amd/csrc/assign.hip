@@ -8,13 +8,21 @@
 // come in as uint32 draws u and pick entry floor(u * c / 2^32) of c
 // candidates in ascending order.
 //
-// One thread per token: the per-token work is integer and bitmask logic.
-// A prep kernel turns the replica map holds[G][E] into one node bitmask per
-// expert and one rank bitmask per (expert, node).  The cover search runs over
-// the nodes that hold some remote expert of the token only (a minimal cover
-// never contains another node), with Gosper's next-combination so masks come
-// in (popcount, value) order and the first feasible mask is the answer;
-// nodes forced by single-node experts are taken before the search.
+// One wave per token.  Lane k < K holds slot k: its expert, the nodes
+// holding that expert and, at the end, its node and rank draws, so the
+// per-slot work and its loads run side by side.  A prep kernel turns the
+// replica map holds[G][E] into one node bitmask per expert and one rank
+// bitmask per (expert, node).  Nodes forced by single-node experts are taken
+// first; the remaining experts' candidate nodes (M of them; a minimal cover
+// never contains another node) are covered by the smallest subset, smallest
+// value first.  Up to M = 12 the wave tests all 2^M subsets, 64 at a time
+// (lane j takes subset base + j), and a wave minimum of (popcount, index)
+// over the feasible ones picks the same subset as enumerating them in that
+// order; above it the wave walks them in order with Gosper's
+// next-combination.  The subset index maps to nodes in ascending order, so
+// index order is node-mask order.  (A thread per token, as before, left one
+// wave per CU at 16K tokens and each wave waited for its slowest token's
+// search: 32 us against 8 us for the DeepSeek-V3 shape.)
 #include "moe_internal.h"
 
 namespace moe {
@@ -22,21 +30,33 @@ namespace {
 
 // Per expert: the nodes holding it, and per (expert, node) the ranks of
 // that node holding it (bit j = rank node*per_node + j; per_node <= 64).
-__global__ void expert_tables_kernel(const uint8_t *__restrict__ holds, int E,
-                                     int G, int N, int per_node,
-                                     uint64_t *__restrict__ nodes,
-                                     uint64_t *__restrict__ rank_bits) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= E) return;
-  uint64_t m = 0;
-  for (int n = 0; n < N; ++n) {
-    uint64_t rb = 0;
-    for (int j = 0; j < per_node; ++j)
-      if (holds[(size_t)(n * per_node + j) * E + e]) rb |= 1ull << j;
-    rank_bits[(size_t)e * N + n] = rb;
-    if (rb) m |= 1ull << n;
+// One wave per expert, lane n < N for node n (N <= 64): the lane gathers
+// its node's per_node flags, and a ballot of the non-empty lanes is the
+// expert's node mask.
+__global__ __launch_bounds__(256) void expert_tables_kernel(
+    const uint8_t *__restrict__ holds, int E, int G, int N, int per_node,
+    uint64_t *__restrict__ nodes, uint64_t *__restrict__ rank_bits) {
+  const int lane = threadIdx.x % kWave;
+  const int e = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (e >= E) return;  // one expert per wave: uniform exit
+  uint64_t rb = 0;
+  if (lane < N) {
+    const uint8_t *h = holds + (size_t)lane * per_node * E + e;
+    int j = 0;
+    for (; j + 8 <= per_node; j += 8) {  // 8 independent loads at a time
+      uint8_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = h[(size_t)(j + q) * E];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (v[q]) rb |= 1ull << (j + q);
+    }
+    for (; j < per_node; ++j)
+      if (h[(size_t)j * E]) rb |= 1ull << j;
+    rank_bits[(size_t)e * N + lane] = rb;
   }
-  nodes[e] = m;
+  const uint64_t m = __ballot(rb != 0);
+  if (lane == 0) nodes[e] = m;
 }
 
 __device__ __forceinline__ int pick(uint32_t u, int c) {
@@ -63,110 +83,143 @@ __device__ __forceinline__ uint64_t expand(uint64_t c, uint64_t uni) {
   return b;
 }
 
-// KT >= K (slots k >= K are ignored); per_node <= 64.
+// 64-bit value of lane `src`, wave-uniform.
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int src) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1)
+    v = min(v, (uint32_t)__shfl_xor((int)v, off));
+  return v;
+}
+
+__device__ __forceinline__ int wave_or(int v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v |= __shfl_xor(v, off);
+  return v;
+}
+
+constexpr int kParallelCoverM = 12;  // test all 2^M subsets up to this M
+
+// One wave per token; KT >= K (<= 32) slots, lane k < K holds slot k.
 template <int KT>
-__global__ __launch_bounds__(64) void assign_kernel(
+__global__ __launch_bounds__(256) void assign_kernel(
     const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ src_rank,
     const uint64_t *__restrict__ enodes, const uint64_t *__restrict__ rbits,
     const uint32_t *__restrict__ u_node, const uint32_t *__restrict__ u_rank,
     int32_t *__restrict__ assign_rank, uint64_t *__restrict__ remote_mask,
     int T, int E, int K, int G, int N, int32_t *__restrict__ err) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;  // one token per wave: uniform exit
   const int per_node = G / N;
   const int sr = src_rank[t];
-  int bad = 0;
-  if ((unsigned)sr >= (unsigned)G) bad |= MOE_DEVERR_SRC_RANK;
+  int bad = (unsigned)sr >= (unsigned)G ? MOE_DEVERR_SRC_RANK : 0;
   const int sn = bad ? 0 : sr / per_node;
   const uint64_t self = 1ull << sn;
-
-  uint64_t m[KT];
-  uint32_t in_u = 0;  // bit k: expert k has no replica on the source node
-#pragma unroll
-  for (int k = 0; k < KT; ++k) {
-    m[k] = 0;
-    if (k < K) {
-      const int e = topk_idx[(size_t)t * K + k];
-      uint64_t nodes = 0;
-      if ((unsigned)e >= (unsigned)E) {
-        bad |= MOE_DEVERR_EXPERT_RANGE;
-      } else {
-        nodes = enodes[e];
-        if (nodes == 0) bad |= MOE_DEVERR_NO_REPLICA;
-      }
-      m[k] = nodes & ~self;
-      if (!(nodes & self)) in_u |= 1u << k;
+  const bool mine = lane < K;  // this lane holds a slot
+  const size_t i = (size_t)t * K + (mine ? lane : 0);
+  int e = 0;
+  uint64_t nodes = 0;
+  uint32_t un = 0, ur = 0;
+  if (mine) {  // all of the slot's loads go out together
+    e = topk_idx[i];
+    un = u_node[i];
+    ur = u_rank[i];
+    if ((unsigned)e >= (unsigned)E) {
+      bad |= MOE_DEVERR_EXPERT_RANGE;
+    } else {
+      nodes = enodes[e];
+      if (nodes == 0) bad |= MOE_DEVERR_NO_REPLICA;
     }
   }
+  bad = wave_or(bad);
   if (bad) {
-    atomicOr(err, bad);
-    for (int k = 0; k < K; ++k) assign_rank[(size_t)t * K + k] = -1;
-    remote_mask[t] = 0;
+    if (lane == 0) {
+      atomicOr(err, bad);
+      remote_mask[t] = 0;
+    }
+    if (mine) assign_rank[i] = -1;
     return;
   }
+  const uint64_t m = nodes & ~self;  // remote nodes holding the expert
+  const bool remote = mine && !(nodes & self);
+  const uint32_t in_u = (uint32_t)__ballot(remote);  // K <= 32
+  uint64_t mk[KT];  // every slot's remote nodes, wave-uniform
+#pragma unroll
+  for (int k = 0; k < KT; ++k) mk[k] = readlane64(m, k);
 
-  // Step 1: smallest cover of the remote experts, by (popcount, value).
-  // A remote expert held by one remote node forces that node into every
-  // cover: those nodes (forced) are taken first, and only the experts they
-  // leave uncovered are searched, over the nodes holding them.  Forced and
-  // searched nodes are disjoint, so (popcount, value) order of the searched
-  // part is the order of the whole mask.  Subsets of the searched nodes are
-  // enumerated as M-bit numbers with Gosper's hack; expanding keeps the
-  // value order.
+  // Nodes forced by experts held on one remote node only, then the experts
+  // they leave uncovered and those experts' candidate nodes.
   uint64_t forced = 0;
 #pragma unroll
   for (int k = 0; k < KT; ++k)
-    if (((in_u >> k) & 1) && __popcll(m[k]) == 1) forced |= m[k];
-  uint32_t left = 0;  // remote experts the forced nodes do not cover
+    if (((in_u >> k) & 1) && __popcll(mk[k]) == 1) forced |= mk[k];
+  uint32_t left = 0;
   uint64_t uni = 0;
 #pragma unroll
   for (int k = 0; k < KT; ++k)
-    if (((in_u >> k) & 1) && !(m[k] & forced)) {
+    if (((in_u >> k) & 1) && !(mk[k] & forced)) {
       left |= 1u << k;
-      uni |= m[k];
+      uni |= mk[k];
     }
   uint64_t best = forced;
   if (left) {
     const int M = __popcll(uni);  // <= 63: the source node's bit is clear
-    bool found = false;
-#pragma unroll 1
-    for (int p = 1; p <= M && !found; ++p) {
-      const uint64_t end = 1ull << M;
-#pragma unroll 1
-      for (uint64_t c = (1ull << p) - 1; c < end;) {
+    if (M <= kParallelCoverM) {
+      uint32_t key = 0xFFFFFFFFu;  // (popcount << 16) | index, feasible only
+      for (int base = 0; base < (1 << M); base += kWave) {
+        const uint32_t c = (uint32_t)(base + lane);
         const uint64_t b = expand(c, uni);
-        bool ok = true;
+        bool ok = c < (1u << M);
 #pragma unroll
         for (int k = 0; k < KT; ++k)
-          if (((left >> k) & 1) && !(b & m[k])) ok = false;
-        if (ok) {
-          best = forced | b;
-          found = true;
-          break;
+          if (((left >> k) & 1) && !(b & mk[k])) ok = false;
+        if (ok) key = min(key, ((uint32_t)__popc(c) << 16) | c);
+      }
+      best = forced | expand(wave_min(key) & 0xFFFFu, uni);
+    } else {
+      // subsets in (popcount, value) order, Gosper's next-combination; the
+      // values are wave-uniform, so every lane walks the same sequence
+      bool found = false;
+#pragma unroll 1
+      for (int p = 1; p <= M && !found; ++p) {
+        const uint64_t end = 1ull << M;
+#pragma unroll 1
+        for (uint64_t c = (1ull << p) - 1; c < end;) {
+          const uint64_t b = expand(c, uni);
+          bool ok = true;
+#pragma unroll
+          for (int k = 0; k < KT; ++k)
+            if (((left >> k) & 1) && !(b & mk[k])) ok = false;
+          if (ok) {
+            best = forced | b;
+            found = true;
+            break;
+          }
+          const uint64_t low = c & (~c + 1);
+          const uint64_t ripple = c + low;
+          c = ripple | (((ripple ^ c) >> 2) >> __builtin_ctzll(low));
         }
-        const uint64_t low = c & (~c + 1);
-        const uint64_t ripple = c + low;
-        c = ripple | (((ripple ^ c) >> 2) >> __builtin_ctzll(low));
       }
     }
   }
-  remote_mask[t] = best;
+  if (lane == 0) remote_mask[t] = best;
 
-  // node, then rank, for every slot (expert and node mask re-read: cache
-  // hits, and the loop needs no per-slot arrays)
-#pragma unroll 1
-  for (int k = 0; k < K; ++k) {
-    const size_t i = (size_t)t * K + k;
-    const int e = topk_idx[i];
-    int node = sn;
-    if ((in_u >> k) & 1) {
-      const uint64_t cand = best & enodes[e] & ~self;
-      node = nth_bit(cand, pick(u_node[i], __popcll(cand)));
-    }
-    const uint64_t rb = rbits[(size_t)e * N + node];
-    assign_rank[i] =
-        node * per_node + nth_bit(rb, pick(u_rank[i], __popcll(rb)));
+  // this lane's slot: a covering node for a remote expert (the source node
+  // otherwise), then a replica rank inside that node
+  if (!mine) return;
+  int node = sn;
+  if (remote) {
+    const uint64_t cand = best & m;
+    node = nth_bit(cand, pick(un, __popcll(cand)));
   }
+  const uint64_t rb = rbits[(size_t)e * N + node];
+  assign_rank[i] = node * per_node + nth_bit(rb, pick(ur, __popcll(rb)));
 }
 
 }  // namespace
@@ -187,14 +240,11 @@ hipError_t launch_assign(const moe_cfg &c, const int32_t *topk_idx,
   uint64_t *enodes = (uint64_t *)((char *)ws + kWsHeader);
   uint64_t *rbits = enodes + c.E;
   const int per_node = c.R / c.N;
-  hipLaunchKernelGGL(expert_tables_kernel, dim3((c.E + 255) / 256),
-                     dim3(256), 0, stream, holds, c.E, c.R, c.N, per_node,
-                     enodes, rbits);
+  hipLaunchKernelGGL(expert_tables_kernel, dim3((c.E + 3) / 4), dim3(256), 0,
+                     stream, holds, c.E, c.R, c.N, per_node, enodes, rbits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.T == 0) return e;
-  // one thread per token, 64-thread workgroups: T/64 waves spread over the
-  // CUs (256-thread workgroups would leave most CUs idle at T = 16K)
-  const dim3 grid((c.T + 63) / 64), block(64);
+  const dim3 grid((c.T + 3) / 4), block(256);  // one wave per token
 #define MOE_ASSIGN(KT_)                                                     \
   hipLaunchKernelGGL((assign_kernel<KT_>), grid, block, 0, stream, topk_idx, \
                      src_rank, enodes, rbits, u_node, u_rank, assign_rank,  \
