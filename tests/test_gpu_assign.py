@@ -99,3 +99,32 @@ def test_assign_device_errors():
     rar, rrm = oracle.assign(idx[ok], src[ok], holds, w.N, un[ok], ur[ok])
     np.testing.assert_array_equal(ar[ok], rar)
     np.testing.assert_array_equal(rm[ok], rrm)
+
+
+def test_assign_both_cover_searches():
+    # 16 nodes and about 3 replicas per expert: about half of the tokens
+    # have more than 12 candidate nodes (the wave walks subsets in order),
+    # the rest at most 12 (the wave tests all subsets at once)
+    w = mi.Workload("cover", T=300, H=8, E=96, K=16, R=32, N=16)
+    holds = mi.replica_layout(w.E, w.R, 2.0, 3)
+    idx = mi.random_topk_idx(w.T, w.E, w.K, seed=3)
+    rng = np.random.Generator(np.random.PCG64(4))
+    src = rng.integers(0, w.R, w.T).astype(np.int32)
+    un, ur = mi.assign_draws(w.T, w.K, 3)
+    ar, rm, err = gpu_assign(w, idx, holds, src, un, ur)
+    assert err == 0
+    rar, rrm = oracle.assign(idx, src, holds, w.N, un, ur)
+    np.testing.assert_array_equal(rm, rrm)
+    np.testing.assert_array_equal(ar, rar)
+    # both searches ran: count candidate nodes per token on the host
+    per_node = w.R // w.N
+    nodes_of = [set((np.nonzero(holds[:, e])[0] // per_node).tolist())
+                for e in range(w.E)]
+    big = 0
+    for t in range(w.T):
+        sn = int(src[t]) // per_node
+        rem = [nodes_of[e] - {sn} for e in idx[t] if sn not in nodes_of[e]]
+        forced = set().union(*[r for r in rem if len(r) == 1]) if rem else set()
+        uni = set().union(*[r for r in rem if not (r & forced)] or [set()])
+        big += len(uni) > 12
+    assert 0 < big < w.T
