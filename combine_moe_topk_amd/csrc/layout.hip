@@ -21,13 +21,15 @@
 //                                            + popcounts of earlier waves
 // which is exactly the token-ascending order inside each expert, with no
 // sorting and no order-dependent atomics.  When all tokens fit in one tile,
-// one workgroup does everything (layout_single_kernel).  Otherwise three
+// one workgroup does everything (layout_block_kernel).  Otherwise three
 // launches:
 //   count: per-tile column counts (experts | ranks | nodes) + node masks
 //   scan : one workgroup turns the count table into per-tile exclusive
 //          prefixes, totals, expert/rank/node offsets
 //   rank : rebuilds the tile bitmaps and writes slot_pos, row_src, node_slot
 // The count table lives in the caller's workspace: nblocks x (E + R + N).
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -278,11 +280,17 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   }
 }
 
-// The whole layout in one workgroup when every token fits in one tile (the
-// decode case): the same LDS bitmaps give the counts, the offsets (scanned in
-// LDS) and the ranks, in one launch instead of three.
+// The whole layout in one workgroup of 1024 threads when every token fits
+// in one tile (the decode case): one launch instead of three.  Thread t
+// takes token t; the 64 tokens t/64 = p share wave bitmap p.  Once the
+// bitmaps are built, thread c turns column c into prefix counts over p,
+// which give every rank directly: rank of (t, e) = expert offset + tokens
+// of e in bitmaps before p + popcount(bitmap p & lanes below).  (The same
+// kernel with 4 tokens per thread, for up to 4096 tokens, was slower than
+// the three launches for the Mixtral shape: 20.5 vs 14.6 us; one CU issues
+// every store.)
 template <int KM>
-__global__ __launch_bounds__(1024) void layout_single_kernel(
+__global__ __launch_bounds__(1024) void layout_block_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
     int per_rank, int per_node_e, int32_t *__restrict__ expert_count,
     int32_t *__restrict__ expert_off, int32_t *__restrict__ rank_count,
@@ -291,26 +299,27 @@ __global__ __launch_bounds__(1024) void layout_single_kernel(
     int32_t *__restrict__ node_off, int32_t *__restrict__ node_slot,
     int32_t *__restrict__ slot_pos, int32_t *__restrict__ row_src,
     int32_t *__restrict__ err) {
-  extern __shared__ uint64_t bm[];  // [W][cols], then the int32 arrays
+  extern __shared__ uint64_t bm[];  // [P][cols], then the int32 arrays
   const int cols = E + R + N;
-  const int W = blockDim.x / kWave;
-  const int w = threadIdx.x / kWave;
+  const int P = (T + kWave - 1) / kWave;  // bitmaps, <= 16
+  const int B = blockDim.x;
   const int lane = threadIdx.x % kWave;
-  int32_t *tot = (int32_t *)(bm + (size_t)W * cols);  // [cols]
+  int32_t *pfx = (int32_t *)(bm + (size_t)P * cols);  // [P][cols]
+  int32_t *tot = pfx + (size_t)P * cols;               // [cols]
   int32_t *eoff = tot + cols;                          // [E + 1]
   int32_t *noff = eoff + E + 1;                        // [N + 1]
+  const uint64_t bit = 1ull << lane;
+  const uint64_t below = bit - 1;
   const int t = threadIdx.x;
   int ev[KM];
   if (t < T) load_ids<KM>(idx + (size_t)t * K, K, ev);
-  for (int i = threadIdx.x; i < W * cols; i += blockDim.x) bm[i] = 0;
+  for (int i = threadIdx.x; i < P * cols; i += B) bm[i] = 0;
   __syncthreads();
 
-  const uint64_t bit = 1ull << lane;
-  const uint64_t below = bit - 1;
-  uint64_t *mine = bm + (size_t)w * cols;
-  uint64_t mask = 0;
   int bad = 0;
-  if (t < T) {
+  if (t < T) {  // set the bitmaps' bits
+    uint64_t *mine = bm + (size_t)(t / kWave) * cols;
+    uint64_t mask = 0;
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
       if (k >= K) break;
@@ -332,18 +341,23 @@ __global__ __launch_bounds__(1024) void layout_single_kernel(
   raise_error(err, bad);
   __syncthreads();
 
-  for (int c = threadIdx.x; c < cols; c += blockDim.x) {
-    int s = 0;
-    for (int v = 0; v < W; ++v) s += __popcll(bm[(size_t)v * cols + c]);
-    tot[c] = s;
+  for (int c = threadIdx.x; c < cols; c += B) {  // prefix counts over p
+    int run = 0;
+#pragma unroll 8
+    for (int q = 0; q < P; ++q) {
+      const int x = __popcll(bm[(size_t)q * cols + c]);
+      pfx[(size_t)q * cols + c] = run;
+      run += x;
+    }
+    tot[c] = run;
   }
   __syncthreads();
   block_exclusive_scan(tot, E, eoff);  // ends with a barrier
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  for (int e = threadIdx.x; e < E; e += B) {
     expert_count[e] = tot[e];
     expert_off[e] = eoff[e];
   }
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+  for (int r = threadIdx.x; r < R; r += B) {
     rank_off[r] = eoff[r * per_rank];
     rank_count[r] = eoff[(r + 1) * per_rank] - eoff[r * per_rank];
     if (rank_token_count) rank_token_count[r] = tot[E + r];
@@ -363,35 +377,38 @@ __global__ __launch_bounds__(1024) void layout_single_kernel(
   }
   __syncthreads();
 
-  if (t >= T) return;
-  int sp[KM];  // ranks first, then the stores (as in the rank kernel)
+  if (t < T) {  // the ranks
+    const size_t p = t / kWave;
+    const uint64_t *mine = bm + p * cols;
+    const int32_t *before = pfx + p * cols;
+    int sp[KM];
+    uint64_t mask = 0;
 #pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    const int e = ev[k];
-    int s = -1;
-    if (k < K && (unsigned)e < (unsigned)E) {
-      s = eoff[e] + __popcll(mine[e] & below);
-      for (int v = 0; v < w; ++v) s += __popcll(bm[(size_t)v * cols + e]);
-    }
-    sp[k] = s;
-  }
-#pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    if (k < K) {
-      const size_t i = (size_t)t * K + k;
-      slot_pos[i] = sp[k];
-      if (sp[k] >= 0) row_src[sp[k]] = (int32_t)i;
-    }
-  }
-  if (node_slot) {
-    for (int n = 0; n < N; ++n) {
+    for (int k = 0; k < KM; ++k) {
+      const int e = ev[k];
       int s = -1;
-      if (mask >> n & 1) {
-        s = noff[n] + __popcll(mine[E + R + n] & below);
-        for (int v = 0; v < w; ++v)
-          s += __popcll(bm[(size_t)v * cols + E + R + n]);
+      if (k < K && (unsigned)e < (unsigned)E) {
+        s = eoff[e] + before[e] + __popcll(mine[e] & below);
+        mask |= 1ull << (e / per_node_e);
       }
-      node_slot[(size_t)t * N + n] = s;
+      sp[k] = s;
+    }
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k < K) {
+        const size_t i = (size_t)t * K + k;
+        slot_pos[i] = sp[k];
+        if (sp[k] >= 0) row_src[sp[k]] = (int32_t)i;
+      }
+    }
+    if (node_slot) {
+      for (int n = 0; n < N; ++n) {
+        const int c = E + R + n;
+        node_slot[(size_t)t * N + n] =
+            (mask >> n & 1)
+                ? noff[n] + before[c] + __popcll(mine[c] & below)
+                : -1;
+      }
     }
   }
 }
@@ -432,11 +449,11 @@ hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
 
   if (g.nblocks == 1) {
     // every token in one tile: one workgroup does the whole layout
-    const int waves = (c.T + kWave - 1) / kWave;
-    const size_t lds = (size_t)waves * g.cols * 8 +
+    const int P = (c.T + kWave - 1) / kWave;
+    const size_t lds = (size_t)P * g.cols * 12 +
                        (size_t)(g.cols + c.E + 1 + c.N + 1) * 4;
     if (lds <= (size_t)kLdsBudget) {
-      hipLaunchKernelGGL(layout_single_kernel<KM>, dim3(1), dim3(waves * kWave),
+      hipLaunchKernelGGL((layout_block_kernel<KM>), dim3(1), dim3(1024),
                          lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
                          per_rank, per_node_e, lay.expert_count,
                          lay.expert_off, lay.rank_count, lay.rank_off,
