@@ -219,19 +219,27 @@ __global__ __launch_bounds__(256) void combine_fp8_kernel(
 // workgroups of one thread per 16-code unit (U16 <= 1024), G tokens at a
 // time reduced (A at a time) into LDS staging laid out like out's rows,
 // then written as one burst of non-temporal stores.  Measured on MI355X:
-// 259 against 264 us for the DeepSeek-V3 shape, 871 against 882 us for the
+// 247 against 264 us for the DeepSeek-V3 shape, 871 against 882 us for the
 // Kimi K2 shape; the FP8 rows are half the bytes of bf16 ones, so the
 // output writes are a smaller share to gain on than in the bf16 combine.
-constexpr int kFp8BurstVecs = 7168;  // 112 KiB of LDS staging per workgroup
+// SV is the LDS staging in 16-byte vectors.  Below K = 16 it is 56 KiB, so
+// two workgroups share a CU and one reduces while the other writes (247
+// against 259 us with 112 KiB at K = 8); at K = 16 the 112 KiB stage of 8
+// tokens is faster (871 against 898 us).
 constexpr size_t kFp8BurstMinBytes = size_t(512) << 20;  // y rows
 
-template <bool OB, int KT, int A>
+template <int KT>
+constexpr int fp8_burst_vecs() {
+  return KT >= 16 ? 7168 : 3584;
+}
+
+template <bool OB, int KT, int A, int SV>
 __global__ __launch_bounds__(1024) void combine_fp8_burst_kernel(
     const char *__restrict__ y, const int32_t *__restrict__ slot_pos,
     const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
     const float *__restrict__ scale, char *__restrict__ out, int T, int U16,
     int H, int L16, int rb, int G, int rows) {
-  __shared__ u32x4 stage[kFp8BurstVecs];
+  __shared__ u32x4 stage[SV];
   constexpr int kOV = OB ? 2 : 4;  // 16-byte output vectors per unit
   const int lane = threadIdx.x % kWave;
   const int u = threadIdx.x;
@@ -354,12 +362,14 @@ hipError_t launch_comb_k(const moe_cfg &c, int B, const void *y,
   constexpr int UPT = fp8_upt<KT>();
   const int U16 = c.H / 16;
   if constexpr (KT > 0 && KT <= 16) {
-    if (U16 <= 1024 && (size_t)c.T * c.K * rb >= kFp8BurstMinBytes) {
-      const int ov = OB ? 2 : 4;
-      const int G = std::min(8, kFp8BurstVecs / (U16 * ov));  // >= 1
+    constexpr int kSV = fp8_burst_vecs<KT>();
+    const int ov = OB ? 2 : 4;
+    if (U16 <= 1024 && U16 * ov <= kSV &&
+        (size_t)c.T * c.K * rb >= kFp8BurstMinBytes) {
+      const int G = std::min(8, kSV / (U16 * ov));  // >= 1: one token fits
       const int ngroups = (c.T + G - 1) / G;
       constexpr int kA = KT >= 16 ? 1 : (16 / KT > 4 ? 4 : 16 / KT);  // rows in flight
-      hipLaunchKernelGGL((combine_fp8_burst_kernel<OB, KT, kA>),
+      hipLaunchKernelGGL((combine_fp8_burst_kernel<OB, KT, kA, kSV>),
                          dim3(std::min(ngroups, 1024)),
                          dim3((U16 + kWave - 1) / kWave * kWave), 0, s,
                          (const char *)y, slot_pos, w, idx, scale, (char *)out,

@@ -158,10 +158,14 @@ def test_combine_fp8(w):
 
 
 # From 512 MiB of FP8 rows the combine switches to its burst kernel (groups
-# of 8 tokens staged in LDS): 20001 tokens leave a ragged last group.
-@functools.lru_cache(maxsize=1)
-def _burst_case():
-    w = mi.Workload("fp8_burst_ragged", T=20001, H=4096, E=64, K=8, R=16,
+# of up to 8 tokens staged in LDS, as many as fit): 20002 tokens leave a
+# ragged last group both for bf16 outputs (7 tokens a group at H = 4096,
+# K = 8) and for fp32 ones (3 a group).  At H = 16384 one bf16 token fills a
+# group of its own and an fp32 token no longer fits the stage, so that
+# combine takes the one-token-a-workgroup kernel.
+@functools.lru_cache(maxsize=2)
+def _burst_case(H=4096, T=20002):
+    w = mi.Workload("fp8_burst_ragged", T=T, H=H, E=64, K=8, R=16,
                     N=4, x_dtype=mi.BF16)
     B = 128
     d = mi.make_inputs(w)
@@ -173,9 +177,10 @@ def _burst_case():
     return w, B, d, idx, wt, lay, send, exact
 
 
+@pytest.mark.parametrize("H,T", [(4096, 20002), (16384, 4001)])
 @pytest.mark.parametrize("odt", [mi.BF16, mi.F32])
-def test_combine_fp8_burst_ragged(odt):
-    w, B, d, idx, wt, lay, send, exact = _burst_case()
+def test_combine_fp8_burst_ragged(odt, H, T):
+    w, B, d, idx, wt, lay, send, exact = _burst_case(H, T)
     w = w.replace(out_dtype=odt)
     assert w.T * w.K * moe.moe_fp8_row_bytes(w.H, B) >= 512 << 20
     out = torch.empty((w.T, w.H), dtype=out_dtype(w), device="cuda")
