@@ -152,7 +152,8 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
   // a column and takes its rows 16 at a time: the 16 loads are issued
   // before any store (stores to the table would otherwise order every later
   // load behind them), so a chunk costs one memory round trip.  (Chunks of
-  // 64 were slower: 9.8 against 6.9 us for 64 tiles.)
+  // 64 were slower: 9.8 against 6.9 us for 64 tiles; so were 64 or 32 rows
+  // a chunk with unconditional clamped loads, 1 or 2 columns a thread.)
   constexpr int kChunk = 16;
   for (int c = threadIdx.x; c < cols; c += blockDim.x) {
     int run = 0;
