@@ -234,6 +234,15 @@ def extras(w, step, stream, alg, dev) -> dict:
         ver = open("/opt/rocm/.info/version").read().strip()
     except OSError:
         pass
+    driver = None
+    try:
+        driver = open("/sys/module/amdgpu/version").read().strip()
+    except OSError:
+        drv = run(["rocm-smi", "--showdriverversion", "--json"])
+        try:
+            driver = next(iter(json.loads(drv).values())).get("Driver version")
+        except (TypeError, ValueError, StopIteration, AttributeError):
+            driver = None
     med_w = _pct(warm, 50)
     return {
         "warm_ms": {"p10": _pct(warm, 10), "p50": med_w, "p90": _pct(warm, 90)},
@@ -243,7 +252,7 @@ def extras(w, step, stream, alg, dev) -> dict:
                           "p90": _pct(clean, 90)},
         "copy_ceiling_gbps": copy_gbps,
         "frac_of_copy_ceiling": alg / (med_w * 1e-3) / 1e9 / copy_gbps,
-        "rocm": ver, "torch": torch.__version__,
+        "rocm": ver, "driver": driver, "torch": torch.__version__,
         "clocks": clocks,
     }
 
@@ -413,10 +422,13 @@ def main() -> int:
             moe.moe_combine(cfg, send, lay.slot_pos, wt, idx, scale, out, stream)
             e[4].record(stream)
         torch.cuda.synchronize()
-        steps_ms = {nm: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
-                                       for i in range(n)]))
-                    for j, nm in enumerate(names)}
+        per = {nm: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(n)]
+               for j, nm in enumerate(names)}
+        steps_ms = {nm: float(np.mean(v)) for nm, v in per.items()}
         result["steps_ms"] = steps_ms
+        result["steps_pct_ms"] = {nm: {"p10": _pct(v, 10), "p50": _pct(v, 50),
+                                       "p90": _pct(v, 90)}
+                                  for nm, v in per.items()}
         kb = kernel_bytes(w)
         dom = max(("pack", "combine"), key=lambda k: steps_ms[k])
         achieved = kb[dom] / (steps_ms[dom] * 1e-3) / 1e9
