@@ -53,7 +53,7 @@ __device__ __forceinline__ void load_ids(const int32_t *row, int K,
 template <int KM>
 __global__ __launch_bounds__(1024) void layout_count_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
-    int per_rank, int per_node_e, uint64_t *__restrict__ node_mask,
+    uint32_t m_rank, uint32_t m_node, uint64_t *__restrict__ node_mask,
     int32_t *__restrict__ table, int32_t *__restrict__ err) {
   extern __shared__ uint64_t bm[];  // [W][cols]
   const int cols = E + R + N;
@@ -81,8 +81,8 @@ __global__ __launch_bounds__(1024) void layout_count_kernel(
       }
       const uint64_t old = atomicOr((unsigned long long *)&mine[e], bit);
       if (old & bit) bad |= MOE_DEVERR_DUP_EXPERT;
-      atomicOr((unsigned long long *)&mine[E + e / per_rank], bit);
-      mask |= 1ull << (e / per_node_e);
+      atomicOr((unsigned long long *)&mine[E + div_small(e, m_rank)], bit);
+      mask |= 1ull << div_small(e, m_node);
     }
     for (uint64_t m = mask; m; m &= m - 1)
       atomicOr((unsigned long long *)&mine[E + R + __ffsll((long long)m) - 1],
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
 template <int KM>
 __global__ __launch_bounds__(1024) void layout_rank_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
-    int per_node_e, const int32_t *__restrict__ table,
+    uint32_t m_node, const int32_t *__restrict__ table,
     int32_t *__restrict__ slot_pos,
     int32_t *__restrict__ row_src, int32_t *__restrict__ node_slot) {
   extern __shared__ uint64_t sm[];
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
       const int e = ev[k];
       if ((unsigned)e >= (unsigned)E) continue;
       atomicOr((unsigned long long *)&mine[e], bit);
-      mask |= 1ull << (e / per_node_e);
+      mask |= 1ull << div_small(e, m_node);
     }
     if (node_slot)
       for (uint64_t m = mask; m; m &= m - 1)
@@ -293,7 +293,8 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
 template <int KM>
 __global__ __launch_bounds__(1024) void layout_block_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
-    int per_rank, int per_node_e, int32_t *__restrict__ expert_count,
+    int per_rank, uint32_t m_rank, uint32_t m_node,
+    int32_t *__restrict__ expert_count,
     int32_t *__restrict__ expert_off, int32_t *__restrict__ rank_count,
     int32_t *__restrict__ rank_off, int32_t *__restrict__ rank_token_count,
     uint64_t *__restrict__ node_mask, int32_t *__restrict__ node_count,
@@ -331,8 +332,8 @@ __global__ __launch_bounds__(1024) void layout_block_kernel(
       }
       const uint64_t old = atomicOr((unsigned long long *)&mine[e], bit);
       if (old & bit) bad |= MOE_DEVERR_DUP_EXPERT;
-      atomicOr((unsigned long long *)&mine[E + e / per_rank], bit);
-      mask |= 1ull << (e / per_node_e);
+      atomicOr((unsigned long long *)&mine[E + div_small(e, m_rank)], bit);
+      mask |= 1ull << div_small(e, m_node);
     }
     for (uint64_t m = mask; m; m &= m - 1)
       atomicOr((unsigned long long *)&mine[E + R + __ffsll((long long)m) - 1],
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(1024) void layout_block_kernel(
       int s = -1;
       if (k < K && (unsigned)e < (unsigned)E) {
         s = eoff[e] + before[e] + __popcll(mine[e] & below);
-        mask |= 1ull << (e / per_node_e);
+        mask |= 1ull << div_small(e, m_node);
       }
       sp[k] = s;
     }
@@ -445,7 +446,8 @@ hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
   int32_t *err = (int32_t *)ws;
   int32_t *table = (int32_t *)((char *)ws + kWsHeader);
   const int per_rank = c.E / c.R;
-  const int per_node_e = c.E / c.N;
+  const uint32_t m_rank = div_magic(per_rank);
+  const uint32_t m_node = div_magic(c.E / c.N);
   const int threads = g.tile_tokens;
 
   if (g.nblocks == 1) {
@@ -456,7 +458,7 @@ hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
     if (lds <= (size_t)kLdsBudget) {
       hipLaunchKernelGGL((layout_block_kernel<KM>), dim3(1), dim3(1024),
                          lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
-                         per_rank, per_node_e, lay.expert_count,
+                         per_rank, m_rank, m_node, lay.expert_count,
                          lay.expert_off, lay.rank_count, lay.rank_off,
                          lay.rank_token_count, lay.node_mask, lay.node_count,
                          lay.node_off, lay.node_slot, lay.slot_pos,
@@ -468,7 +470,7 @@ hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
     const size_t lds = (size_t)g.tile_waves * g.cols * 8;
     hipLaunchKernelGGL(layout_count_kernel<KM>, dim3(g.nblocks), dim3(threads),
                        lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
-                       per_rank, per_node_e, lay.node_mask, table, err);
+                       m_rank, m_node, lay.node_mask, table, err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -489,7 +491,7 @@ hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
                        (size_t)(c.E + c.N) * 4;
     hipLaunchKernelGGL(layout_rank_kernel<KM>, dim3(g.nblocks), dim3(threads),
                        lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
-                       per_node_e, table, lay.slot_pos,
+                       m_node, table, lay.slot_pos,
                        lay.row_src, lay.node_slot);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -19,6 +19,18 @@ constexpr int kMaxLevels = MOE_MAX_LEVELS;  // capacity / bucket levels
 // 16-byte vector used for every row copy (one global_load/store_dwordx4).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Quotient n / d for 0 <= n, d and n * d < 2^31 (expert ids and experts per
+// rank or node, both at most 4096) as one 32x32->64 multiply and a shift, in
+// place of the dozen-instruction division sequence a runtime divisor costs.
+// With m = ceil(2^31 / d) = 2^31 / d + f (0 <= f < 1) and n = q d + r:
+// n m / 2^31 = q + r / d + n f / 2^31 < q + (d - 1) / d + 1 / d = q + 1.
+inline uint32_t div_magic(int d) {
+  return (uint32_t)(((1ull << 31) + (uint64_t)d - 1) / (uint64_t)d);
+}
+__device__ __forceinline__ int div_small(int n, uint32_t m) {
+  return (int)(((uint64_t)(uint32_t)n * m) >> 31);
+}
+
 // Launch geometry of the three layout kernels.  A layout workgroup owns a
 // tile of `tile_tokens` consecutive tokens, one token per lane, and keeps one
 // 64-bit token bitmap per (wave, expert / rank / node) in LDS.
