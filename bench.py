@@ -596,8 +596,11 @@ def fp8_path(args, w, cfg, x, lg, scale, idx, wt, lay, out, ws,
 
     b, ob = w.elem_bytes, w.out_elem_bytes
     T, H, K = w.T, w.H, w.K
-    kb = {"pack_fp8": T * H * b + T * K * rb + 4 * T * K,
-          "combine_fp8": T * K * rb + T * H * ob + 12 * T * K + 4 * w.E}
+    # a row's payload is its codes and block scales; the padding up to the
+    # 128-byte stride is not part of what the method moves
+    pay = H + 4 * (H // B)
+    kb = {"pack_fp8": T * H * b + T * K * pay + 4 * T * K,
+          "combine_fp8": T * K * pay + T * H * ob + 12 * T * K + 4 * w.E}
     meta = T * (4 * w.E + 32 * K + 8) + 8 * (w.E + w.R + w.N)
     alg = kb["pack_fp8"] + kb["combine_fp8"] + meta - 4 * T * K - 12 * T * K
     n = max(args.steps, 5)

@@ -8,13 +8,19 @@
 // format and block size are readings: OCP E4M3 codes (gfx950's native FP8
 // conversions), one fp32 scale s = amax/448 per block of B elements, codes
 // of fp32(x * fp32(448/amax)) clamped to +-448.  A packed row is H codes,
-// then H/B scales, then zero padding to a multiple of 16 bytes.
+// then H/B scales, then zero padding to a multiple of 128 bytes, so rows
+// start on 128-byte lines and no line holds parts of two rows.  Against a
+// 16-byte stride (7392 against 7424 bytes for H = 7168, B = 128) the step
+// of the DeepSeek-V3 shape took 480 instead of 503 us on MI355X: a row
+// read or written no longer shares its first and last lines with the
+// neighbouring rows, which other waves touch at other times.
 //
 // Pack: one wave per token.  A lane holds 8 consecutive elements of the row
 // (one 16-byte bf16 vector); the B/8 lanes of a block reduce its amax with
 // xor-shuffles, every lane converts its 8 elements with v_cvt_pk_fp8_f32 and
-// the wave stores the codes (8 bytes a lane) and the block scales to the K
-// destination rows.  The row is read once and quantised once per token.
+// the wave stores the codes (8 bytes a lane) and then the row's tail (block
+// scales and padding, gathered in LDS) to the K destination rows.  The row
+// is read once and quantised once per token.
 //
 // Combine: as the bf16 combine, with 16 codes (one 16-byte vector) and their
 // block scale per unit; codes are widened with v_cvt_pk_f32_fp8 and
@@ -27,6 +33,8 @@
 namespace moe {
 namespace {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // E4M3 codes of 4 fp32 values, packed little-endian in one word.
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c,
                                            float d) {
@@ -36,23 +44,35 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c,
 }
 
 // L = B/8 lanes per block; VPL units of 8 elements per lane and pass.
+// Codes go out as 8-byte stores, 512 contiguous bytes per instruction.  The
+// row's tail (block scales, then zero padding up to the 128-byte row
+// stride) is gathered in LDS, nd dwords per wave, and stored as whole
+// dwords, so every line of a row is written in full by one wave.  Ordinary
+// stores: with the 128-byte stride the pack took 212 us for the DeepSeek-V3
+// shape against 248 us with device-scope non-temporal stores and 255 us with
+// non-temporal ones (the combine after it then reads 25 us faster, which
+// does not make up for it).
 template <bool XB, int L, int VPL>
 __global__ __launch_bounds__(256) void pack_fp8_kernel(
     const char *__restrict__ x, const int32_t *__restrict__ slot_pos,
     char *__restrict__ send, int T, int K, int U, int H, int rb, int rows) {
+  extern __shared__ float tail_lds[];  // [4 waves][nd]
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  const int w = threadIdx.x / kWave;
+  const int t = blockIdx.x * (256 / kWave) + w;
   if (t >= T) return;  // one token per wave: uniform exit
   const int my_slot = lane < K ? slot_pos[(size_t)t * K + lane] : -1;
   const char *xrow = x + (size_t)t * U * (XB ? 16 : 32);
+  const int nd = (rb - H) / 4;  // tail dwords: U / L scales, then padding
+  float *tl = tail_lds + (size_t)w * nd;
+  for (int q = U / L + lane; q < nd; q += kWave) tl[q] = 0.0f;
 
   for (int base = 0; base < U; base += kWave * VPL) {
     Unit<XB> u[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j)
       u[j].load(xrow, min(base + j * kWave + lane, U - 1));
-    uint32_t c0[VPL], c1[VPL];
-    float sc[VPL];
+    u32x2 code[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       float a = 0.0f;
@@ -63,7 +83,8 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(
       // whole blocks of their own and are never stored
 #pragma unroll
       for (int off = 1; off < L; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-      sc[j] = a / 448.0f;
+      const int i = base + j * kWave + lane;
+      if (lane % L == 0 && i < U) tl[i / L] = a / 448.0f;
       const float r = 448.0f / a;
       float p[8];
 #pragma unroll
@@ -72,38 +93,31 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(
         // a block of zeros keeps its zeros (and their signs)
         p[e] = a == 0.0f ? v : fminf(fmaxf(v * r, -448.0f), 448.0f);
       }
-      c0[j] = e4m3x4(p[0], p[1], p[2], p[3]);
-      c1[j] = e4m3x4(p[4], p[5], p[6], p[7]);
+      code[j][0] = e4m3x4(p[0], p[1], p[2], p[3]);
+      code[j][1] = e4m3x4(p[4], p[5], p[6], p[7]);
     }
     for (int k = 0; k < K; ++k) {
       const int s = __builtin_amdgcn_readlane(my_slot, k);
       if ((unsigned)s >= (unsigned)rows) continue;  // out-of-range: skipped
-      char *dst = send + (size_t)s * rb;
+      u32x2 *dst = (u32x2 *)(send + (size_t)s * rb);
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         const int i = base + j * kWave + lane;
-        if (i < U) {
-          uint32_t *cw = (uint32_t *)(dst + (size_t)i * 8);
-          cw[0] = c0[j];
-          cw[1] = c1[j];
-          if (lane % L == 0) *(float *)(dst + H + 4 * (i / L)) = sc[j];
-        }
+        if (i < U) dst[i] = code[j];
       }
     }
   }
-}
-
-// Zero the padding words of every used send row once: a row is rb bytes, of
-// which [H + 4H/B, rb) are padding (at most 12 bytes).
-__global__ void pad_fp8_kernel(const int32_t *__restrict__ slot_pos,
-                               char *__restrict__ send, int n, int used,
-                               int rb, int rows) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int s = slot_pos[i];
-  if ((unsigned)s >= (unsigned)rows) return;
-  for (int b = used; b < rb; b += 4)
-    *(uint32_t *)(send + (size_t)s * rb + b) = 0u;
+  // the tail's LDS words were written by other lanes of this wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int k = 0; k < K; ++k) {
+    const int s = __builtin_amdgcn_readlane(my_slot, k);
+    if ((unsigned)s >= (unsigned)rows) continue;
+    float *dst = (float *)(send + (size_t)s * rb + H);
+    for (int q = lane; q < nd; q += kWave)
+      dst[q] = tl[q];
+  }
 }
 
 // 16 elements of a unit as fp32 from one 16-byte code vector.
@@ -316,8 +330,9 @@ hipError_t launch_pack_v(const moe_cfg &c, const void *x,
                          const int32_t *slot_pos, void *send, int rb,
                          hipStream_t s) {
   const int U = c.H / 8;
+  const size_t lds = (size_t)4 * ((rb - c.H) / 4) * sizeof(float);
   hipLaunchKernelGGL((pack_fp8_kernel<XB, L, VPL>), dim3((c.T + 3) / 4),
-                     dim3(256), 0, s, (const char *)x, slot_pos,
+                     dim3(256), lds, s, (const char *)x, slot_pos,
                      (char *)send, c.T, c.K, U, c.H, rb, c.T * c.K);
   return hipGetLastError();
 }
@@ -409,7 +424,7 @@ hipError_t launch_comb_d(const moe_cfg &c, int B, const void *y,
 }  // namespace
 
 size_t fp8_row_bytes(int H, int B) {
-  return ((size_t)H + 4 * (size_t)(H / B) + 15) & ~(size_t)15;
+  return ((size_t)H + 4 * (size_t)(H / B) + 127) & ~(size_t)127;
 }
 
 bool fp8_block_ok(const moe_cfg &c, int B) {
@@ -421,15 +436,9 @@ hipError_t launch_pack_fp8(const moe_cfg &c, int B, const void *x,
                            hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
   const int rb = (int)fp8_row_bytes(c.H, B);
-  const int used = c.H + 4 * (c.H / B);
-  hipError_t e = c.x_dtype == MOE_BF16
-                     ? launch_pack_b<true>(c, B, x, slot_pos, send, rb, stream)
-                     : launch_pack_b<false>(c, B, x, slot_pos, send, rb, stream);
-  if (e != hipSuccess || used == rb) return e;
-  const int n = c.T * c.K;
-  hipLaunchKernelGGL(pad_fp8_kernel, dim3((n + 255) / 256), dim3(256), 0,
-                     stream, slot_pos, (char *)send, n, used, rb, n);
-  return hipGetLastError();
+  return c.x_dtype == MOE_BF16
+             ? launch_pack_b<true>(c, B, x, slot_pos, send, rb, stream)
+             : launch_pack_b<false>(c, B, x, slot_pos, send, rb, stream);
 }
 
 hipError_t launch_combine_fp8(const moe_cfg &c, int B, const void *y,

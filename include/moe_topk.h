@@ -270,7 +270,8 @@ int moe_dispatch_combine_nodes(const moe_cfg *cfg, const void *x,
  *                           round to nearest even, sign kept)
  *   bytes [H, H + 4H/B)     one fp32 scale per block of B elements
  *   bytes up to the stride  zero padding; stride = moe_fp8_row_bytes(H, B),
- *                           a multiple of 16
+ *                           a multiple of 128 (no 128-byte block holds
+ *                           parts of two rows)
  * For a block with largest magnitude amax: scale = amax / 448 and
  * code_i = e4m3(min(max(x_i * (448 / amax), -448), 448)), each operation in
  * fp32 with round to nearest even; a block of zeros has scale 0 and zero

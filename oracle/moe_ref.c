@@ -503,8 +503,9 @@ int moe_ref_combine_nodes(int T, int H, int N, int part_dtype,
  *     decided in the precision the kernel uses; a block of zeros has s = 0
  *     and zero codes;
  *   - a packed row is H code bytes followed by the H/B scales (fp32, little
- *     endian), zero-padded to a multiple of 16 bytes so that every row
- *     starts on a 16-byte boundary: round_up(H + 4H/B, 16) bytes;
+ *     endian), zero-padded to a multiple of 128 bytes so that every row
+ *     starts on a 128-byte boundary and no two rows share a 128-byte block:
+ *     round_up(H + 4H/B, 128) bytes;
  *   - dequantised value = code value * s.
  */
 
@@ -575,9 +576,9 @@ static void quant_row(int H, int B, int x_dtype, const void *x, size_t row,
 }
 
 /* Row bytes of the FP8 send buffer: H codes + H/B fp32 scales, rounded up
- * to a multiple of 16. */
+ * to a multiple of 128. */
 size_t moe_ref_fp8_row_bytes(int H, int B) {
-  return ((size_t)H + 4 * (size_t)(H / B) + 15) & ~(size_t)15;
+  return ((size_t)H + 4 * (size_t)(H / B) + 127) & ~(size_t)127;
 }
 
 /* Pack with quantisation: every token's row is quantised once and written

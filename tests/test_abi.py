@@ -175,8 +175,9 @@ def test_capacity_entry_points_validate_on_host():
     assert lib.moe_dispatch_layout_capacity(ctypes.byref(c), None, lv, 9,
                                             ctypes.byref(lay), None, 0,
                                             None) == moe.MOE_EINVAL
-    assert moe.moe_fp8_row_bytes(7168, 128) == 7168 + 224
-    assert moe.moe_fp8_row_bytes(256, 128) == 272
+    assert moe.moe_fp8_row_bytes(7168, 128) == 7424     # 7168 + 224, to 128
+    assert moe.moe_fp8_row_bytes(256, 128) == 384      # 256 + 8, to 128
+    assert moe.moe_fp8_row_bytes(7168, 32) == 8064     # 7168 + 896, exact
     assert moe.moe_fp8_row_bytes(100, 32) == 0
 
 

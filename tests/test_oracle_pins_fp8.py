@@ -122,7 +122,7 @@ def test_pack_fp8_equals_independent_quantisation(xdt, B):
     idx, _ = oracle.gate(d["logits"], w.K)
     lay = oracle.layout(idx, w.E, w.R, w.N)
     send = oracle.pack_fp8(x, lay["slot_pos"], B)
-    rb = -(-(w.H + 4 * w.H // B) // 16) * 16
+    rb = -(-(w.H + 4 * w.H // B) // 128) * 128   # rows on 128-byte blocks
     assert send.shape == (w.T * w.K, rb)
     assert not send[:, w.H + 4 * w.H // B:].any()  # zero padding
     codes, scales = oracle.fp8_rows_split(send, w.H, B)
