@@ -428,7 +428,11 @@ size_t fp8_row_bytes(int H, int B) {
 }
 
 bool fp8_block_ok(const moe_cfg &c, int B) {
-  return (B == 32 || B == 64 || B == 128) && c.H % B == 0 && c.H % 16 == 0;
+  if (!(B == 32 || B == 64 || B == 128) || c.H % B != 0 || c.H % 16 != 0)
+    return false;
+  // the pack keeps each of its 4 waves' row tail (H/B scales and up to 32
+  // padding words) in LDS: at most 64 KiB a workgroup
+  return (fp8_row_bytes(c.H, B) - (size_t)c.H) * 4 <= 65536;
 }
 
 hipError_t launch_pack_fp8(const moe_cfg &c, int B, const void *x,

@@ -265,7 +265,9 @@ int moe_dispatch_combine_nodes(const moe_cfg *cfg, const void *x,
  * (Dispatch)": tokens travel with block scale factors; "Workload-Static
  * Optical Circuit Switching for Scalable LLM Inference Decode",
  * "Communication precision": FP8 transport for MoE dispatch.  Format of a
- * packed row (qblock B in {32, 64, 128}, H % B == 0, H % 16 == 0):
+ * packed row (qblock B in {32, 64, 128}, H % B == 0, H % 16 == 0, and a row
+ * tail of scales and padding of at most 16 KiB, about H/B <= 4064; other
+ * shapes give MOE_EUNSUPPORTED):
  *   bytes [0, H)            OCP E4M3 codes (bias 7, largest magnitude 448,
  *                           round to nearest even, sign kept)
  *   bytes [H, H + 4H/B)     one fp32 scale per block of B elements

@@ -179,6 +179,13 @@ def test_capacity_entry_points_validate_on_host():
     assert moe.moe_fp8_row_bytes(256, 128) == 384      # 256 + 8, to 128
     assert moe.moe_fp8_row_bytes(7168, 32) == 8064     # 7168 + 896, exact
     assert moe.moe_fp8_row_bytes(100, 32) == 0
+    # the FP8 pack holds each row's scale-and-padding tail in LDS: a tail
+    # above 16 KiB (H/B scales of 4 bytes) is refused on the host
+    for H, B, code in ((7168, 32, moe.MOE_EINVAL), (131072, 32, moe.MOE_EINVAL),
+                       (131200, 32, moe.MOE_EUNSUPPORTED)):
+        c = cfg(T=4, H=H)
+        assert lib.moe_dispatch_pack_fp8(ctypes.byref(c), None, None, B, None,
+                                         None) == code, (H, B)
 
 
 def test_assign_entry_point_validates_on_host():
