@@ -278,7 +278,7 @@ def test_fp8_fused_full_size(w):
 @pytest.mark.parametrize("T,H,E,K,R,N,xdt,odt", [
     (1, 128, 8, 2, 4, 2, mi.BF16, mi.BF16),
     (97, 96, 24, 3, 6, 3, mi.F32, mi.F32),        # generic K, B = 32
-    (130, 256, 16, 16, 16, 16, mi.BF16, mi.F32),  # padded stride (264 -> 272)
+    (130, 256, 16, 16, 16, 16, mi.BF16, mi.F32),  # padded stride (264 -> 384)
     (65, 1056, 64, 5, 8, 8, mi.BF16, mi.BF16),    # ragged rows, B = 32
 ])
 def test_fp8_edge_shapes(T, H, E, K, R, N, xdt, odt):
