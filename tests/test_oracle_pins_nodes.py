@@ -69,7 +69,8 @@ def test_pack_nodes_multiset(w):
 
 def test_pack_nodes_dedup_bound():
     # the crossings of a token never exceed min(K, N), and a token always
-    # crosses to at least ceil(K / (E/N)) nodes (the benchmark spec bound)
+    # crosses to at least ceil(K / (E/N)) nodes (a token's K experts span
+    # at least that many nodes of E/N experts each)
     for w in SHAPES:
         _, _, _, lay = _route(w)
         pc = _popcount(lay["node_mask"])
