@@ -149,6 +149,32 @@ def test_layout_without_optional_outputs():
     check_layout(res, ref)
 
 
+def test_layout_struct_follows_replaced_tensors():
+    # the binding keeps a layout's C struct between calls; a field that now
+    # holds another tensor (or None) must reach the library on the next call
+    w = mi.QWEN3.replace(T=999)
+    idx, _ = oracle.gate(mi.make_inputs(w, with_x=False)["logits"], w.K)
+    ref = oracle.layout(idx, w.E, w.R, w.N)
+    cfg = cfg_of(w)
+    lay = moe.alloc_layout(cfg)
+    ws = moe.alloc_workspace(cfg)
+    ids = dev(idx.reshape(-1))
+    moe.moe_dispatch_layout(cfg, ids, lay, ws)
+    old = lay.slot_pos
+    old.fill_(-7)
+    lay.slot_pos = torch.full_like(old, -9)
+    lay.node_slot = None
+    moe.moe_dispatch_layout(cfg, ids, lay, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(lay.slot_pos).reshape(w.T, w.K),
+                                  ref["slot_pos"])
+    assert bool((old == -7).all())
+    lay.node_slot = torch.empty(w.T * w.N, dtype=torch.int32, device="cuda")
+    moe.moe_dispatch_layout(cfg, ids, lay, ws)
+    np.testing.assert_array_equal(host(lay.node_slot).reshape(w.T, w.N),
+                                  ref["node_slot"])
+
+
 # ----------------------------------------------------------------- pack ----
 
 @pytest.mark.parametrize("w", SMALL, ids=_ids)
