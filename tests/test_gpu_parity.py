@@ -194,10 +194,16 @@ def test_pack(w):
 # last piece per row (375 16-byte vectors, pieces of 128) and an odd K.
 LARGE_RAGGED = mi.Workload("large_ragged", T=40000, H=3000, E=60, K=5, R=15,
                            N=5, x_dtype=mi.BF16, out_dtype=mi.BF16)
+# Wider tokens: K = 20 and K = 32 put 10 and 16 waves on each piece of x,
+# spread over several workgroups.
+LARGE_WIDE = [mi.Workload("large_k20", T=3800, H=7168, E=40, K=20, R=8, N=4,
+                          x_dtype=mi.BF16, out_dtype=mi.BF16),
+              mi.Workload("large_k32", T=2400, H=7168, E=64, K=32, R=16, N=8,
+                          x_dtype=mi.BF16, out_dtype=mi.BF16)]
 
 
-def test_pack_large_ragged():
-    w = LARGE_RAGGED
+@pytest.mark.parametrize("w", [LARGE_RAGGED] + LARGE_WIDE, ids=_ids)
+def test_pack_large_ragged(w):
     assert w.T * w.K * w.H * 2 >= 1 << 30
     x = mi.random_x(w.T, w.H, w.x_dtype, seed=3)
     idx = mi.random_topk_idx(w.T, w.E, w.K, seed=3)
