@@ -261,6 +261,7 @@ hipError_t launch_g(int C, const float *logits, int32_t *idx, float *w,
     case 16: return launch_gc<G, 16>(logits, idx, w, T, E, K, renorm, s);
     case 32: return launch_gc<G, 32>(logits, idx, w, T, E, K, renorm, s);
     case 48: return launch_gc<G, 48>(logits, idx, w, T, E, K, renorm, s);
+    case 56: return launch_gc<G, 56>(logits, idx, w, T, E, K, renorm, s);
     case 64: return launch_gc<G, 64>(logits, idx, w, T, E, K, renorm, s);
     default: return hipErrorInvalidValue;
   }
@@ -282,7 +283,9 @@ hipError_t launch_gate(const moe_cfg &c, const float *logits,
   while (G < 64 && ((c.E + G - 1) / G > 64 || G < c.K)) G <<= 1;
   if (c.T <= kGateWaveTokens) G = 64;
   const int need = (c.E + G - 1) / G;  // keys per lane, <= 64
-  int C = need <= 2 ? pow2_ceil(need) : (need <= 32 ? pow2_ceil(need) : (need <= 48 ? 48 : 64));
+  // keys per lane: a power of two up to 32, then 48, 56 or 64 (56 is the
+  // Kimi K2 shape, E = 896 over 16 lanes: no dead key slots)
+  int C = need <= 32 ? pow2_ceil(need) : (need <= 48 ? 48 : (need <= 56 ? 56 : 64));
   if (C < 1) C = 1;
   const int renorm = (c.flags & MOE_F_NO_RENORM) ? 0 : 1;
   switch (G) {

@@ -71,9 +71,22 @@ ADV = [("all_equal", lambda T, E, K: mi.logits_all_equal(T, E)),
 
 @pytest.mark.parametrize("name,make", ADV, ids=[a[0] for a in ADV])
 @pytest.mark.parametrize("E,K", [(8, 1), (8, 8), (16, 3), (64, 16),
-                                 (256, 8), (896, 16), (1000, 32), (4096, 5)])
+                                 (256, 8), (896, 16), (1000, 32), (3500, 8),
+                                 (4096, 5)])
 def test_gate_ties(name, make, E, K):
     T = 300
+    w = mi.Workload("adv", T=T, H=8, E=E, K=K, R=1, N=1)
+    lg = make(T, E, K)
+    ref_idx, ref_w = oracle.gate(lg, K)
+    idx, wt = gpu_gate(w, lg)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
+@pytest.mark.parametrize("name,make", ADV, ids=[a[0] for a in ADV])
+@pytest.mark.parametrize("E,K", [(64, 16), (256, 8), (896, 16), (1700, 20)])
+def test_gate_ties_many_tokens(name, make, E, K):
+    # above 1024 tokens a token takes 16 or 32 lanes instead of a wave
+    T = 2000
     w = mi.Workload("adv", T=T, H=8, E=E, K=K, R=1, N=1)
     lg = make(T, E, K)
     ref_idx, ref_w = oracle.gate(lg, K)
