@@ -153,7 +153,10 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(
   // before any store (stores to the table would otherwise order every later
   // load behind them), so a chunk costs one memory round trip.  (Chunks of
   // 64 were slower: 9.8 against 6.9 us for 64 tiles; so were 64 or 32 rows
-  // a chunk with unconditional clamped loads, 1 or 2 columns a thread.)
+  // a chunk with unconditional clamped loads, 1 or 2 columns a thread; two
+  // chunk buffers used in turn, each chunk's loads issued before the
+  // previous chunk's stores, changed nothing: 23.2 against 22.6 us for the
+  // whole DeepSeek-V3 layout, 45.4 against 45.6 us for Kimi K2.)
   constexpr int kChunk = 16;
   for (int c = threadIdx.x; c < cols; c += blockDim.x) {
     int run = 0;
