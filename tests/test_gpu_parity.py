@@ -316,9 +316,14 @@ def test_fused_small(w):
               w.out_dtype)
 
 
-@pytest.mark.parametrize("w", FULL, ids=_ids)
-def test_fused_full_size(w):
-    d = mi.make_inputs(w)
+@pytest.mark.parametrize("w,seed", [(w, None) for w in FULL] +
+                         [(mi.DEEPSEEK_V3, 1), (mi.QWEN3, 1)],
+                         ids=lambda v: _ids(v) if isinstance(v, mi.Workload)
+                         else f"seed{v}")
+def test_fused_full_size(w, seed):
+    # every workload at its full size with its seed, and seed 1 as a rerun
+    # of the clustered and the Zipf-skewed logits
+    d = mi.make_inputs(w, seed=seed)
     res = run_fused(w, d, keep_device=True)
     assert res["dev_error"] == 0
     idx, wt = oracle.gate(d["logits"], w.K)
