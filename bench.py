@@ -50,6 +50,10 @@ KERNEL_SOURCES = {
     "combine": ["combine_moe_topk_amd/csrc/combine.hip",
                 "combine_moe_topk_amd/csrc/row_io.h"],
     "assign": ["combine_moe_topk_amd/csrc/assign.hip"],
+    "pack_fp8": ["combine_moe_topk_amd/csrc/fp8.hip",
+                 "combine_moe_topk_amd/csrc/row_io.h"],
+    "combine_fp8": ["combine_moe_topk_amd/csrc/fp8.hip",
+                    "combine_moe_topk_amd/csrc/row_io.h"],
 }
 # int32 vector ALU issue rate: 256 CUs x 64 lanes x 2.4 GHz (lane-ops/s)
 ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
@@ -67,6 +71,21 @@ def kernel_bytes(w: mi.Workload) -> dict:
     }
 
 
+def fp8_kernel_bytes(w: mi.Workload, B: int = 128) -> dict:
+    """Algorithmic bytes per launch of the FP8 pack and combine.  A row's
+    payload is its H codes and H/B fp32 scales; the padding up to the
+    128-byte row stride is not part of what the method moves."""
+    b, ob = w.elem_bytes, w.out_elem_bytes
+    T, H, K = w.T, w.H, w.K
+    pay = H + 4 * (H // B)
+    return {
+        # x read once, K quantised rows written, slot positions read
+        "pack_fp8": T * H * b + T * K * pay + 4 * T * K,
+        # K quantised rows read, one row written, routing read, scales
+        "combine_fp8": T * K * pay + T * H * ob + 12 * T * K + 4 * w.E,
+    }
+
+
 def two_leg_kernel_bytes(w: mi.Workload, D: int, pb: int) -> dict:
     """Algorithmic bytes per launch of the two-leg kernels; D = crossings."""
     b, ob = w.elem_bytes, w.out_elem_bytes
@@ -81,6 +100,19 @@ def two_leg_kernel_bytes(w: mi.Workload, D: int, pb: int) -> dict:
         # partial rows read, one output row written, node slots read
         "sum_nodes": D * H * pb + T * H * ob + 4 * T * N,
     }
+
+
+def copy_calibration(mib: int, dev) -> None:
+    """Three device copies of mib MiB: under rocprofv3 --pmc they give the
+    counters' reading for a known number of bytes read and written."""
+    import torch
+
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def source_digest(paths) -> str:
@@ -444,15 +476,8 @@ def main() -> int:
             result["roofline"][f"{k}_gbps"] = kb[k] / (steps_ms[k] * 1e-3) / 1e9
 
     if args.copy_calib_mib > 0:
-        nb = args.copy_calib_mib << 20
-        src = torch.ones(nb, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calib_bytes"] = nb
-        del src, dst
+        copy_calibration(args.copy_calib_mib, dev)
+        result["copy_calib_bytes"] = args.copy_calib_mib << 20
 
     if not args.fused_only and not args.no_extras:
         result["extras"] = extras(w, step, stream, alg, dev)
@@ -551,7 +576,8 @@ def two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out, ws,
         "steps_ms": steps_ms,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic(dom, w.name),
                      "alg_bytes_per_launch": kb[dom],
                      "launch_ms": steps_ms[dom],
                      **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
@@ -594,13 +620,8 @@ def fp8_path(args, w, cfg, x, lg, scale, idx, wt, lay, out, ws,
     ms = ev0.elapsed_time(ev1) / args.steps
     print(f"bench: fp8 {ms:.4f} ms/step", file=sys.stderr, flush=True)
 
-    b, ob = w.elem_bytes, w.out_elem_bytes
     T, H, K = w.T, w.H, w.K
-    # a row's payload is its codes and block scales; the padding up to the
-    # 128-byte stride is not part of what the method moves
-    pay = H + 4 * (H // B)
-    kb = {"pack_fp8": T * H * b + T * K * pay + 4 * T * K,
-          "combine_fp8": T * K * pay + T * H * ob + 12 * T * K + 4 * w.E}
+    kb = fp8_kernel_bytes(w, B)
     meta = T * (4 * w.E + 32 * K + 8) + 8 * (w.E + w.R + w.N)
     alg = kb["pack_fp8"] + kb["combine_fp8"] + meta - 4 * T * K - 12 * T * K
     n = max(args.steps, 5)
@@ -641,12 +662,16 @@ def fp8_path(args, w, cfg, x, lg, scale, idx, wt, lay, out, ws,
         "steps_ms": steps_ms,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic(dom, w.name),
                      "alg_bytes_per_launch": kb[dom],
                      "launch_ms": steps_ms[dom],
                      **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
                         for k in kb}},
     }
+    if args.copy_calib_mib > 0:
+        copy_calibration(args.copy_calib_mib, x.device)
+        result["copy_calib_bytes"] = args.copy_calib_mib << 20
     print(json.dumps(result), flush=True)
     return 0
 
@@ -734,7 +759,8 @@ def capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream) -> int:
         "steps_ms": steps_ms,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": load_traffic(dom, w.name),
                      "alg_bytes_per_launch": kb[dom],
                      "launch_ms": steps_ms[dom],
                      **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9

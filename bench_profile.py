@@ -66,7 +66,7 @@ def _counter(db: str):
 
 
 def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
-            cmd_fetch: str, cmd_write: str) -> None:
+            cmd_fetch: str, cmd_write: str, kind: str = "flat") -> None:
     fr, wr = _counter(fetch_db), _counter(write_db)
     calib = calib_mib * 1024.0  # KiB read and written by the copy
 
@@ -86,10 +86,14 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
 
     fk, wk = per_kernel(fr), per_kernel(wr)
     w = bench.mi.WORKLOADS[workload]
-    alg = bench.kernel_bytes(w)
+    if kind == "fp8":
+        alg, roles = bench.fp8_kernel_bytes(w), ("pack_fp8", "combine_fp8")
+    else:
+        alg, roles = bench.kernel_bytes(w), ("pack", "combine")
     path = os.path.join(PROFILES, "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
-    md = [f"# HBM traffic per launch: {workload}\n",
+    name = workload if kind == "flat" else f"{workload}_{kind}"
+    md = [f"# HBM traffic per launch: {name}\n",
           "Commands:\n", f"    {cmd_fetch}", f"    {cmd_write}\n",
           f"Calibration: a device copy of {calib_mib} MiB reads "
           f"{calib / f_scale / 1024:.1f} MiB as FETCH_SIZE and "
@@ -100,7 +104,7 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
     for k in sorted(fk, key=lambda k: -(fk[k] + wk.get(k, 0))):
         fb = fk[k] * 1024 * f_scale
         wb = wk.get(k, 0.0) * 1024 * w_scale
-        role = next((r for r in ("pack", "combine") if k.startswith(r)), None)
+        role = next((r for r in roles if k.startswith(r + "_")), None)
         a = alg.get(role) if role else None
         md.append(f"{k:42s} {fk[k] / 1024:10.1f} {wk.get(k, 0) / 1024:10.1f} "
                   f"{(fb + wb) / 1e6:10.1f} "
@@ -116,7 +120,7 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
     md.append("```\n")
     with open(path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
-    with open(os.path.join(PROFILES, f"hbm_traffic_{workload}.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"hbm_traffic_{name}.md"), "w") as f:
         f.write("\n".join(md))
 
 
@@ -200,6 +204,7 @@ def main() -> None:
     r.add_argument("--calib-mib", type=int, required=True)
     r.add_argument("--cmd-fetch", required=True)
     r.add_argument("--cmd-write", required=True)
+    r.add_argument("--path", default="flat", choices=("flat", "fp8"))
     a = ap.parse_args()
     if a.what == "trace":
         trace(a.db, a.out, a.cmd)
@@ -209,7 +214,7 @@ def main() -> None:
         valu(a.db, a.workload, a.cmd)
     else:
         traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
-                a.cmd_write)
+                a.cmd_write, a.path)
 
 
 if __name__ == "__main__":

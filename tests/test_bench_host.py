@@ -40,6 +40,15 @@ def test_deepseek_bytes_per_launch():
     assert abs(w.algorithmic_bytes() / 1e6 - 4249.0) < 0.1
 
 
+def test_fp8_bytes_per_launch():
+    # payload of a row: H one-byte codes and H/128 fp32 scales, not padding
+    w = mi.DEEPSEEK_V3
+    kb = bench.fp8_kernel_bytes(w, 128)
+    T, H, K = w.T, w.H, w.K
+    assert kb["pack_fp8"] == T * H * 2 + T * K * (H + 4 * H // 128) + 4 * T * K
+    assert kb["combine_fp8"] == T * K * 7392 + T * H * 2 + 12 * T * K + 4 * w.E
+
+
 def test_alu_peak():
     # 256 CUs x 64 lanes x 2.4 GHz
     assert bench.ALU_PEAK_TOPS == pytest.approx(39.3216)
