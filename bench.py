@@ -50,6 +50,12 @@ KERNEL_SOURCES = {
     "combine": ["combine_moe_topk_amd/csrc/combine.hip",
                 "combine_moe_topk_amd/csrc/row_io.h"],
     "assign": ["combine_moe_topk_amd/csrc/assign.hip"],
+    "pack_nodes": ["combine_moe_topk_amd/csrc/pack.hip"],
+    "forward": ["combine_moe_topk_amd/csrc/nodes.hip"],
+    "partial": ["combine_moe_topk_amd/csrc/nodes.hip",
+                "combine_moe_topk_amd/csrc/row_io.h"],
+    "sum_nodes": ["combine_moe_topk_amd/csrc/nodes.hip",
+                  "combine_moe_topk_amd/csrc/row_io.h"],
     "pack_fp8": ["combine_moe_topk_amd/csrc/fp8.hip",
                  "combine_moe_topk_amd/csrc/row_io.h"],
     "combine_fp8": ["combine_moe_topk_amd/csrc/fp8.hip",
@@ -583,6 +589,9 @@ def two_leg(args, w, d, cfg, x, lg, scale, idx, wt, lay, send, out, ws,
                      **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
                         for k in kb}},
     }
+    if args.copy_calib_mib > 0:
+        copy_calibration(args.copy_calib_mib, dev)
+        result["copy_calib_bytes"] = args.copy_calib_mib << 20
     print(json.dumps(result), flush=True)
     return 0
 

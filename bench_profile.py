@@ -66,7 +66,8 @@ def _counter(db: str):
 
 
 def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
-            cmd_fetch: str, cmd_write: str, kind: str = "flat") -> None:
+            cmd_fetch: str, cmd_write: str, kind: str = "flat",
+            crossings: int = 0, part_bytes: int = 2) -> None:
     fr, wr = _counter(fetch_db), _counter(write_db)
     calib = calib_mib * 1024.0  # KiB read and written by the copy
 
@@ -86,10 +87,19 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
 
     fk, wk = per_kernel(fr), per_kernel(wr)
     w = bench.mi.WORKLOADS[workload]
+    # role of a kernel: the first prefix its name starts with
     if kind == "fp8":
-        alg, roles = bench.fp8_kernel_bytes(w), ("pack_fp8", "combine_fp8")
+        alg = bench.fp8_kernel_bytes(w)
+        prefixes = {"pack_fp8_": "pack_fp8", "combine_fp8_": "combine_fp8"}
+    elif kind == "two_leg":
+        if crossings <= 0:
+            raise SystemExit("--crossings (dedup.crossing_rows) is required")
+        alg = bench.two_leg_kernel_bytes(w, crossings, part_bytes)
+        prefixes = {"pack_": "pack_nodes", "forward_": "forward",
+                    "partial_": "partial", "sum_nodes_": "sum_nodes"}
     else:
-        alg, roles = bench.kernel_bytes(w), ("pack", "combine")
+        alg = bench.kernel_bytes(w)
+        prefixes = {"pack_": "pack", "combine_": "combine"}
     path = os.path.join(PROFILES, "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     name = workload if kind == "flat" else f"{workload}_{kind}"
@@ -104,7 +114,8 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
     for k in sorted(fk, key=lambda k: -(fk[k] + wk.get(k, 0))):
         fb = fk[k] * 1024 * f_scale
         wb = wk.get(k, 0.0) * 1024 * w_scale
-        role = next((r for r in roles if k.startswith(r + "_")), None)
+        role = next((r for pre, r in prefixes.items() if k.startswith(pre)),
+                    None)
         a = alg.get(role) if role else None
         md.append(f"{k:42s} {fk[k] / 1024:10.1f} {wk.get(k, 0) / 1024:10.1f} "
                   f"{(fb + wb) / 1e6:10.1f} "
@@ -204,7 +215,11 @@ def main() -> None:
     r.add_argument("--calib-mib", type=int, required=True)
     r.add_argument("--cmd-fetch", required=True)
     r.add_argument("--cmd-write", required=True)
-    r.add_argument("--path", default="flat", choices=("flat", "fp8"))
+    r.add_argument("--path", default="flat", choices=("flat", "fp8", "two_leg"))
+    r.add_argument("--crossings", type=int, default=0,
+                   help="two_leg: (token, node) crossings of the run")
+    r.add_argument("--part-bytes", type=int, default=2,
+                   help="two_leg: bytes per partial element (bf16 2, f32 4)")
     a = ap.parse_args()
     if a.what == "trace":
         trace(a.db, a.out, a.cmd)
@@ -214,7 +229,7 @@ def main() -> None:
         valu(a.db, a.workload, a.cmd)
     else:
         traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
-                a.cmd_write, a.path)
+                a.cmd_write, a.path, a.crossings, a.part_bytes)
 
 
 if __name__ == "__main__":
