@@ -56,6 +56,10 @@ KERNEL_SOURCES = {
                 "combine_moe_topk_amd/csrc/row_io.h"],
     "sum_nodes": ["combine_moe_topk_amd/csrc/nodes.hip",
                   "combine_moe_topk_amd/csrc/row_io.h"],
+    "pack_capacity": ["combine_moe_topk_amd/csrc/pack.hip",
+                      "combine_moe_topk_amd/csrc/capacity.hip"],
+    "combine_capacity": ["combine_moe_topk_amd/csrc/combine.hip",
+                         "combine_moe_topk_amd/csrc/row_io.h"],
     "pack_fp8": ["combine_moe_topk_amd/csrc/fp8.hip",
                  "combine_moe_topk_amd/csrc/row_io.h"],
     "combine_fp8": ["combine_moe_topk_amd/csrc/fp8.hip",
@@ -89,6 +93,21 @@ def fp8_kernel_bytes(w: mi.Workload, B: int = 128) -> dict:
         "pack_fp8": T * H * b + T * K * pay + 4 * T * K,
         # K quantised rows read, one row written, routing read, scales
         "combine_fp8": T * K * pay + T * H * ob + 12 * T * K + 4 * w.E,
+    }
+
+
+def capacity_kernel_bytes(w: mi.Workload, C: int, dropped: int) -> dict:
+    """Algorithmic bytes per launch of the capacity path's pack (its used
+    rows and its zeroed padding rows, two kernels) and combine; C = rows a
+    segment holds, dropped = (token, slot) pairs over capacity."""
+    b, ob = w.elem_bytes, w.out_elem_bytes
+    T, H, K = w.T, w.H, w.K
+    n_rows, kept = w.E * C, T * K - dropped
+    return {
+        # x read once, every padded row written, slots and row sources read
+        "pack_capacity": T * H * b + n_rows * H * b + 4 * T * K + 4 * n_rows,
+        # kept rows read, one row written, routing read
+        "combine_capacity": kept * H * b + T * H * ob + 12 * T * K,
     }
 
 
@@ -718,11 +737,8 @@ def capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream) -> int:
     print(f"bench: capacity {ms:.4f} ms/step, C={C}, dropped {dropped}",
           file=sys.stderr, flush=True)
 
-    b, ob = w.elem_bytes, w.out_elem_bytes
     T, H, K = w.T, w.H, w.K
-    kept = T * K - dropped
-    kb = {"pack_capacity": T * H * b + n_rows * H * b + 4 * T * K + 4 * n_rows,
-          "combine_capacity": kept * H * b + T * H * ob + 12 * T * K}
+    kb = capacity_kernel_bytes(w, C, dropped)
     meta = T * (4 * w.E + 32 * K + 8) + 8 * w.E
     alg = kb["pack_capacity"] + kb["combine_capacity"] + meta
     n = max(args.steps, 5)
@@ -775,6 +791,9 @@ def capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream) -> int:
                      **{f"{k}_gbps": kb[k] / (steps_ms[k] * 1e-3) / 1e9
                         for k in kb}},
     }
+    if args.copy_calib_mib > 0:
+        copy_calibration(args.copy_calib_mib, x.device)
+        result["copy_calib_bytes"] = args.copy_calib_mib << 20
     print(json.dumps(result), flush=True)
     return 0
 

@@ -67,7 +67,8 @@ def _counter(db: str):
 
 def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
             cmd_fetch: str, cmd_write: str, kind: str = "flat",
-            crossings: int = 0, part_bytes: int = 2) -> None:
+            crossings: int = 0, part_bytes: int = 2, capacity: int = 0,
+            dropped: int = 0) -> None:
     fr, wr = _counter(fetch_db), _counter(write_db)
     calib = calib_mib * 1024.0  # KiB read and written by the copy
 
@@ -97,6 +98,13 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
         alg = bench.two_leg_kernel_bytes(w, crossings, part_bytes)
         prefixes = {"pack_": "pack_nodes", "forward_": "forward",
                     "partial_": "partial", "sum_nodes_": "sum_nodes"}
+    elif kind == "capacity":
+        if capacity <= 0:
+            raise SystemExit("--capacity (config.capacity) is required")
+        alg = bench.capacity_kernel_bytes(w, capacity, dropped)
+        # the padded pack is two kernels: used rows, then zeroed padding
+        prefixes = {"pack_": "pack_capacity", "zero_rows_": "pack_capacity",
+                    "combine_": "combine_capacity"}
     else:
         alg = bench.kernel_bytes(w)
         prefixes = {"pack_": "pack", "combine_": "combine"}
@@ -111,23 +119,40 @@ def traffic(fetch_db: str, write_db: str, workload: str, calib_mib: int,
           f"scaled by {f_scale:.3f} (fetch) and {w_scale:.3f} (write).\n",
           "```",
           f"{'kernel':42s} {'fetch MiB':>10s} {'write MiB':>10s} {'scaled MB':>10s} {'alg MB':>10s} {'ratio':>6s}"]
+    def role_of(k):
+        return next((r for pre, r in prefixes.items() if k.startswith(pre)),
+                    None)
+
+    kernels_of = {}
+    for k in fk:
+        if role_of(k):
+            kernels_of.setdefault(role_of(k), []).append(k)
     for k in sorted(fk, key=lambda k: -(fk[k] + wk.get(k, 0))):
         fb = fk[k] * 1024 * f_scale
         wb = wk.get(k, 0.0) * 1024 * w_scale
-        role = next((r for pre, r in prefixes.items() if k.startswith(pre)),
-                    None)
-        a = alg.get(role) if role else None
+        role = role_of(k)
+        # a ratio per kernel only where the role is this one kernel
+        a = alg.get(role) if role and len(kernels_of[role]) == 1 else None
         md.append(f"{k:42s} {fk[k] / 1024:10.1f} {wk.get(k, 0) / 1024:10.1f} "
                   f"{(fb + wb) / 1e6:10.1f} "
                   f"{(a / 1e6 if a else float('nan')):10.1f} "
                   f"{((fb + wb) / a if a else float('nan')):6.3f}")
-        if role:
-            data[f"{role}/{workload}"] = {
-                "kernel": k, "bytes_per_launch": fb + wb, "fetch_bytes": fb,
-                "write_bytes": wb, "alg_bytes": a,
-                "fetch_scale": f_scale, "write_scale": w_scale,
-                "source_sha": bench.source_digest(bench.KERNEL_SOURCES[role]),
-            }
+    for role, ks in sorted(kernels_of.items()):
+        fb = sum(fk[k] for k in ks) * 1024 * f_scale
+        wb = sum(wk.get(k, 0.0) for k in ks) * 1024 * w_scale
+        a = alg.get(role)
+        if len(ks) > 1:
+            md.append(f"{role + ' (all its kernels)':42s} "
+                      f"{sum(fk[k] for k in ks) / 1024:10.1f} "
+                      f"{sum(wk.get(k, 0) for k in ks) / 1024:10.1f} "
+                      f"{(fb + wb) / 1e6:10.1f} {a / 1e6:10.1f} "
+                      f"{(fb + wb) / a:6.3f}")
+        data[f"{role}/{workload}"] = {
+            "kernel": " + ".join(sorted(ks)), "bytes_per_launch": fb + wb,
+            "fetch_bytes": fb, "write_bytes": wb, "alg_bytes": a,
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "source_sha": bench.source_digest(bench.KERNEL_SOURCES[role]),
+        }
     md.append("```\n")
     with open(path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
@@ -215,11 +240,16 @@ def main() -> None:
     r.add_argument("--calib-mib", type=int, required=True)
     r.add_argument("--cmd-fetch", required=True)
     r.add_argument("--cmd-write", required=True)
-    r.add_argument("--path", default="flat", choices=("flat", "fp8", "two_leg"))
+    r.add_argument("--path", default="flat",
+                   choices=("flat", "fp8", "two_leg", "capacity"))
     r.add_argument("--crossings", type=int, default=0,
                    help="two_leg: (token, node) crossings of the run")
     r.add_argument("--part-bytes", type=int, default=2,
                    help="two_leg: bytes per partial element (bf16 2, f32 4)")
+    r.add_argument("--capacity", type=int, default=0,
+                   help="capacity: rows per segment of the run")
+    r.add_argument("--dropped", type=int, default=0,
+                   help="capacity: dropped (token, slot) pairs of the run")
     a = ap.parse_args()
     if a.what == "trace":
         trace(a.db, a.out, a.cmd)
@@ -229,7 +259,8 @@ def main() -> None:
         valu(a.db, a.workload, a.cmd)
     else:
         traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
-                a.cmd_write, a.path, a.crossings, a.part_bytes)
+                a.cmd_write, a.path, a.crossings, a.part_bytes, a.capacity,
+                a.dropped)
 
 
 if __name__ == "__main__":
