@@ -181,6 +181,25 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, what: str = "") -> Optional[int]
     return t.data_ptr()
 
 
+def _need(t: Optional[torch.Tensor], n: int, what: str) -> None:
+    """Refuse a buffer smaller than the n elements cfg says a call touches.
+
+    The kernels index buffers by cfg alone, so an undersized tensor would be
+    an out-of-bounds device access; this raises before anything is enqueued
+    (and before the device check, so it also holds for host tensors)."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{what}: {t.numel()} elements, the call needs "
+                         f"at least {n}")
+
+
+def _need_rows(t: torch.Tensor, H: int, what: str) -> int:
+    """A [rows, H] buffer whose row count the call takes from its shape."""
+    if t.dim() != 2 or t.shape[1] != H:
+        raise ValueError(f"{what}: expected shape [rows, {H}], got "
+                         f"{list(t.shape)}")
+    return t.shape[0]
+
+
 def _check(rc: int, what: str) -> None:
     if rc != MOE_OK:
         raise MoeError(rc, what)
@@ -209,6 +228,10 @@ def moe_workspace_init(ws: torch.Tensor, stream=None) -> None:
 
 def moe_topk_gate(cfg: moe_cfg, logits: torch.Tensor, topk_idx: torch.Tensor,
                   topk_w: torch.Tensor, stream=None) -> None:
+    TK = cfg.T * cfg.K
+    _need(logits, cfg.T * cfg.E, "logits")
+    _need(topk_idx, TK, "topk_idx")
+    _need(topk_w, TK, "topk_w")
     _check(lib().moe_topk_gate(
         ctypes.byref(cfg), _ptr(logits, torch.float32, "logits"),
         _ptr(topk_idx, torch.int32, "topk_idx"),
@@ -236,18 +259,29 @@ class Layout:
     _cs: Optional[moe_layout] = dataclasses.field(default=None, init=False,
                                                   repr=False, compare=False)
 
-    def c_struct(self) -> moe_layout:
-        """The C struct of these tensors, checked and built again only when
-        a field holds another tensor or other memory than last time."""
+    def c_struct(self, cfg: moe_cfg) -> moe_layout:
+        """The C struct of these tensors, checked (type, device, size for
+        cfg) and built again only when a field holds another tensor or other
+        memory than last time, or cfg's sizes changed."""
         ts = [getattr(self, name) for name in LAYOUT_FIELDS]
-        key = tuple(None if t is None else (id(t), t.data_ptr()) for t in ts)
+        sizes = layout_sizes(cfg)
+        key = (sizes,) + tuple(None if t is None else (id(t), t.data_ptr())
+                               for t in ts)
         if key != self._key:
+            for name, t, n in zip(LAYOUT_FIELDS, ts, sizes):
+                _need(t, n, name)
             vals = []
             for name, t in zip(LAYOUT_FIELDS, ts):
                 want = torch.int64 if name == "node_mask" else torch.int32
                 vals.append(_ptr(t, want, name))
             self._cs, self._key = moe_layout(*vals), key
         return self._cs
+
+
+def layout_sizes(cfg: moe_cfg) -> tuple:
+    """Elements each moe_layout field must hold, in LAYOUT_FIELDS order."""
+    T, E, K, R, N = cfg.T, cfg.E, cfg.K, cfg.R, cfg.N
+    return (E, E + 1, R, R + 1, R, T, N, N + 1, T * N, T * K, T * K)
 
 
 def alloc_layout(cfg: moe_cfg, device="cuda", optional: bool = True) -> Layout:
@@ -282,7 +316,8 @@ def alloc_workspace(cfg: moe_cfg, device="cuda", init: bool = True,
 
 def moe_dispatch_layout(cfg: moe_cfg, topk_idx: torch.Tensor, layout: Layout,
                         ws: torch.Tensor, stream=None) -> None:
-    lay = layout.c_struct()
+    _need(topk_idx, cfg.T * cfg.K, "topk_idx")
+    lay = layout.c_struct(cfg)
     _check(lib().moe_dispatch_layout(
         ctypes.byref(cfg), _ptr(topk_idx, torch.int32, "topk_idx"),
         ctypes.byref(lay), _ptr(ws, torch.uint8, "ws"), ws.numel(),
@@ -295,6 +330,10 @@ def _row_dtype(cfg: moe_cfg):
 
 def moe_dispatch_pack(cfg: moe_cfg, x: torch.Tensor, slot_pos: torch.Tensor,
                       send: torch.Tensor, stream=None) -> None:
+    TK = cfg.T * cfg.K
+    _need(x, cfg.T * cfg.H, "x")
+    _need(slot_pos, TK, "slot_pos")
+    _need(send, TK * cfg.H, "send")
     _check(lib().moe_dispatch_pack(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(slot_pos, torch.int32, "slot_pos"),
@@ -302,10 +341,31 @@ def moe_dispatch_pack(cfg: moe_cfg, x: torch.Tensor, slot_pos: torch.Tensor,
         "moe_dispatch_pack")
 
 
+def _need_routing(cfg: moe_cfg, slot_pos, topk_w, topk_idx, expert_scale):
+    TK = cfg.T * cfg.K
+    _need(slot_pos, TK, "slot_pos")
+    _need(topk_w, TK, "topk_w")
+    _need(topk_idx, TK, "topk_idx")
+    _need(expert_scale, cfg.E, "expert_scale")
+
+
+def _need_front(cfg: moe_cfg, x, logits, expert_scale, topk_idx, topk_w):
+    """Sizes of the inputs and gate outputs of the fused calls."""
+    TK = cfg.T * cfg.K
+    _need(x, cfg.T * cfg.H, "x")
+    _need(logits, cfg.T * cfg.E, "logits")
+    _need(expert_scale, cfg.E, "expert_scale")
+    _need(topk_idx, TK, "topk_idx")
+    _need(topk_w, TK, "topk_w")
+
+
 def moe_combine(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
                 topk_w: torch.Tensor, topk_idx: Optional[torch.Tensor],
                 expert_scale: Optional[torch.Tensor], out: torch.Tensor,
                 stream=None) -> None:
+    _need_routing(cfg, slot_pos, topk_w, topk_idx, expert_scale)
+    _need(y, cfg.T * cfg.K * cfg.H, "y")
+    _need(out, cfg.T * cfg.H, "out")
     _check(lib().moe_combine(
         ctypes.byref(cfg), _ptr(y, _row_dtype(cfg), "y"),
         _ptr(slot_pos, torch.int32, "slot_pos"),
@@ -321,7 +381,10 @@ def moe_dispatch_combine(cfg: moe_cfg, x: torch.Tensor, logits: torch.Tensor,
                          topk_idx: torch.Tensor, topk_w: torch.Tensor,
                          layout: Layout, send: torch.Tensor, out: torch.Tensor,
                          ws: torch.Tensor, stream=None) -> None:
-    lay = layout.c_struct()
+    _need_front(cfg, x, logits, expert_scale, topk_idx, topk_w)
+    _need(send, cfg.T * cfg.K * cfg.H, "send")
+    _need(out, cfg.T * cfg.H, "out")
+    lay = layout.c_struct(cfg)
     _check(lib().moe_dispatch_combine(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(logits, torch.float32, "logits"),
@@ -349,9 +412,16 @@ def _part_code(part: torch.Tensor) -> int:
     raise TypeError(f"part: expected float32 or bfloat16, got {part.dtype}")
 
 
+def _node_rows(cfg: moe_cfg) -> int:
+    return cfg.T * min(cfg.K, cfg.N)
+
+
 def moe_dispatch_pack_nodes(cfg: moe_cfg, x: torch.Tensor,
                             node_slot: torch.Tensor, node_send: torch.Tensor,
                             stream=None) -> None:
+    _need(x, cfg.T * cfg.H, "x")
+    _need(node_slot, cfg.T * cfg.N, "node_slot")
+    _need(node_send, _node_rows(cfg) * cfg.H, "node_send")
     _check(lib().moe_dispatch_pack_nodes(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(node_slot, torch.int32, "node_slot"),
@@ -363,6 +433,12 @@ def moe_dispatch_forward(cfg: moe_cfg, node_send: torch.Tensor,
                          node_slot: torch.Tensor, topk_idx: torch.Tensor,
                          slot_pos: torch.Tensor, send: torch.Tensor,
                          stream=None) -> None:
+    TK = cfg.T * cfg.K
+    _need(node_send, _node_rows(cfg) * cfg.H, "node_send")
+    _need(node_slot, cfg.T * cfg.N, "node_slot")
+    _need(topk_idx, TK, "topk_idx")
+    _need(slot_pos, TK, "slot_pos")
+    _need(send, TK * cfg.H, "send")
     _check(lib().moe_dispatch_forward(
         ctypes.byref(cfg), _ptr(node_send, _row_dtype(cfg), "node_send"),
         _ptr(node_slot, torch.int32, "node_slot"),
@@ -377,6 +453,10 @@ def moe_combine_partial(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
                         expert_scale: Optional[torch.Tensor],
                         node_slot: torch.Tensor, part: torch.Tensor,
                         stream=None) -> None:
+    _need_routing(cfg, slot_pos, topk_w, topk_idx, expert_scale)
+    _need(y, cfg.T * cfg.K * cfg.H, "y")
+    _need(node_slot, cfg.T * cfg.N, "node_slot")
+    _need(part, _node_rows(cfg) * cfg.H, "part")
     _check(lib().moe_combine_partial(
         ctypes.byref(cfg), _ptr(y, _row_dtype(cfg), "y"),
         _ptr(slot_pos, torch.int32, "slot_pos"),
@@ -390,6 +470,9 @@ def moe_combine_partial(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
 def moe_combine_nodes(cfg: moe_cfg, part: torch.Tensor,
                       node_slot: torch.Tensor, out: torch.Tensor,
                       stream=None) -> None:
+    _need(part, _node_rows(cfg) * cfg.H, "part")
+    _need(node_slot, cfg.T * cfg.N, "node_slot")
+    _need(out, cfg.T * cfg.H, "out")
     _check(lib().moe_combine_nodes(
         ctypes.byref(cfg), _ptr(part, None, "part"), _part_code(part),
         _ptr(node_slot, torch.int32, "node_slot"),
@@ -405,7 +488,12 @@ def moe_dispatch_combine_nodes(cfg: moe_cfg, x: torch.Tensor,
                                send: torch.Tensor, part: torch.Tensor,
                                out: torch.Tensor, ws: torch.Tensor,
                                stream=None) -> None:
-    lay = layout.c_struct()
+    _need_front(cfg, x, logits, expert_scale, topk_idx, topk_w)
+    _need(node_send, _node_rows(cfg) * cfg.H, "node_send")
+    _need(send, cfg.T * cfg.K * cfg.H, "send")
+    _need(part, _node_rows(cfg) * cfg.H, "part")
+    _need(out, cfg.T * cfg.H, "out")
+    lay = layout.c_struct(cfg)
     _check(lib().moe_dispatch_combine_nodes(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(logits, torch.float32, "logits"),
@@ -427,9 +515,17 @@ def moe_fp8_row_bytes(H: int, qblock: int = 128) -> int:
     return lib().moe_fp8_row_bytes(H, qblock)
 
 
+def _fp8_rb(cfg: moe_cfg, qblock: int) -> int:
+    # 0 for an unsupported (H, qblock): the C call then refuses it
+    return moe_fp8_row_bytes(cfg.H, qblock)
+
+
 def moe_dispatch_pack_fp8(cfg: moe_cfg, x: torch.Tensor,
                           slot_pos: torch.Tensor, send: torch.Tensor,
                           qblock: int = 128, stream=None) -> None:
+    _need(x, cfg.T * cfg.H, "x")
+    _need(slot_pos, cfg.T * cfg.K, "slot_pos")
+    _need(send, cfg.T * cfg.K * _fp8_rb(cfg, qblock), "send")
     _check(lib().moe_dispatch_pack_fp8(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(slot_pos, torch.int32, "slot_pos"), qblock,
@@ -441,6 +537,9 @@ def moe_combine_fp8(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
                     topk_w: torch.Tensor, topk_idx: Optional[torch.Tensor],
                     expert_scale: Optional[torch.Tensor], out: torch.Tensor,
                     qblock: int = 128, stream=None) -> None:
+    _need_routing(cfg, slot_pos, topk_w, topk_idx, expert_scale)
+    _need(y, cfg.T * cfg.K * _fp8_rb(cfg, qblock), "y")
+    _need(out, cfg.T * cfg.H, "out")
     _check(lib().moe_combine_fp8(
         ctypes.byref(cfg), _ptr(y, torch.uint8, "y"), qblock,
         _ptr(slot_pos, torch.int32, "slot_pos"),
@@ -458,7 +557,10 @@ def moe_dispatch_combine_fp8(cfg: moe_cfg, x: torch.Tensor,
                              layout: Layout, send: torch.Tensor,
                              out: torch.Tensor, ws: torch.Tensor,
                              qblock: int = 128, stream=None) -> None:
-    lay = layout.c_struct()
+    _need_front(cfg, x, logits, expert_scale, topk_idx, topk_w)
+    _need(send, cfg.T * cfg.K * _fp8_rb(cfg, qblock), "send")
+    _need(out, cfg.T * cfg.H, "out")
+    lay = layout.c_struct(cfg)
     _check(lib().moe_dispatch_combine_fp8(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(logits, torch.float32, "logits"),
@@ -484,7 +586,11 @@ class CapacityLayout:
     row_src: torch.Tensor
     dropped: torch.Tensor
 
-    def c_struct(self) -> moe_capacity_layout:
+    def c_struct(self, cfg: moe_cfg, levels) -> moe_capacity_layout:
+        E = cfg.E
+        sizes = (E, E, E + 1, cfg.T * cfg.K, E * int(levels[-1]), 1)
+        for n, k in zip(CAP_FIELDS, sizes):
+            _need(getattr(self, n), k, n)
         return moe_capacity_layout(*[_ptr(getattr(self, n), torch.int32, n)
                                      for n in CAP_FIELDS])
 
@@ -518,7 +624,8 @@ def moe_dispatch_layout_capacity(cfg: moe_cfg, topk_idx: torch.Tensor, levels,
                                  layout: CapacityLayout, ws: torch.Tensor,
                                  stream=None) -> None:
     lv, q = _levels(levels)
-    lay = layout.c_struct()
+    _need(topk_idx, cfg.T * cfg.K, "topk_idx")
+    lay = layout.c_struct(cfg, levels)
     _check(lib().moe_dispatch_layout_capacity(
         ctypes.byref(cfg), _ptr(topk_idx, torch.int32, "topk_idx"), lv, q,
         ctypes.byref(lay), _ptr(ws, torch.uint8, "ws"), ws.numel(),
@@ -528,8 +635,10 @@ def moe_dispatch_layout_capacity(cfg: moe_cfg, topk_idx: torch.Tensor, levels,
 def moe_dispatch_pack_capacity(cfg: moe_cfg, x: torch.Tensor,
                                slot_pos: torch.Tensor, row_src: torch.Tensor,
                                send: torch.Tensor, stream=None) -> None:
-    if row_src.numel() < send.shape[0]:
-        raise ValueError("row_src must have one entry per send row")
+    n_rows = _need_rows(send, cfg.H, "send")
+    _need(row_src, n_rows, "row_src")
+    _need(x, cfg.T * cfg.H, "x")
+    _need(slot_pos, cfg.T * cfg.K, "slot_pos")
     _check(lib().moe_dispatch_pack_capacity(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(slot_pos, torch.int32, "slot_pos"),
@@ -542,6 +651,9 @@ def moe_combine_capacity(cfg: moe_cfg, y: torch.Tensor, slot_pos: torch.Tensor,
                          topk_w: torch.Tensor, topk_idx: Optional[torch.Tensor],
                          expert_scale: Optional[torch.Tensor],
                          out: torch.Tensor, stream=None) -> None:
+    _need_rows(y, cfg.H, "y")
+    _need_routing(cfg, slot_pos, topk_w, topk_idx, expert_scale)
+    _need(out, cfg.T * cfg.H, "out")
     _check(lib().moe_combine_capacity(
         ctypes.byref(cfg), _ptr(y, _row_dtype(cfg), "y"), y.shape[0],
         _ptr(slot_pos, torch.int32, "slot_pos"),
@@ -560,9 +672,11 @@ def moe_dispatch_combine_capacity(cfg: moe_cfg, x: torch.Tensor,
                                   send: torch.Tensor, out: torch.Tensor,
                                   ws: torch.Tensor, stream=None) -> None:
     lv, q = _levels(levels)
-    if send.shape[0] != cfg.E * int(levels[-1]):
+    if _need_rows(send, cfg.H, "send") != cfg.E * int(levels[-1]):
         raise ValueError("send must have E * levels[-1] rows")
-    lay = layout.c_struct()
+    _need_front(cfg, x, logits, expert_scale, topk_idx, topk_w)
+    _need(out, cfg.T * cfg.H, "out")
+    lay = layout.c_struct(cfg, levels)
     _check(lib().moe_dispatch_combine_capacity(
         ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
         _ptr(logits, torch.float32, "logits"),
@@ -596,6 +710,12 @@ def moe_assign_tasks(cfg: moe_cfg, topk_idx: torch.Tensor,
     remote_mask: int64 (bit n = node n)."""
     if holds.numel() != cfg.R * cfg.E:
         raise ValueError("holds must be [R, E]")
+    TK = cfg.T * cfg.K
+    for t, n, what in ((topk_idx, TK, "topk_idx"), (src_rank, cfg.T, "src_rank"),
+                       (u_node, TK, "u_node"), (u_rank, TK, "u_rank"),
+                       (assign_rank, TK, "assign_rank"),
+                       (remote_mask, cfg.T, "remote_mask")):
+        _need(t, n, what)
     _check(lib().moe_assign_tasks(
         ctypes.byref(cfg), _ptr(topk_idx, torch.int32, "topk_idx"),
         _ptr(src_rank, torch.int32, "src_rank"),

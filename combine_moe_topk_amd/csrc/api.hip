@@ -422,7 +422,7 @@ int moe_dispatch_combine_capacity(const moe_cfg *cfg, const void *x,
 }
 
 size_t moe_assign_workspace_bytes(const moe_cfg *cfg) {
-  if (validate(cfg) != MOE_OK) return 0;
+  if (validate(cfg) != MOE_OK || !moe::assign_ok(*cfg)) return 0;
   return moe::assign_ws_bytes(*cfg);
 }
 

@@ -229,7 +229,16 @@ size_t assign_ws_bytes(const moe_cfg &c) {
   return kWsHeader + ((tables + 255) & ~(size_t)255);
 }
 
-bool assign_ok(const moe_cfg &c) { return c.R / c.N <= 64; }
+// At most kMaxAssignNodes nodes: the minimum cover walks subsets of the up
+// to N - 1 remote candidate nodes in size order, so one token may test up to
+// 2^(N-1) of them ("Cobalt: Leveraging Expert Co-activation for Efficient
+// Distributed MoE Training", Section 3.3, gives the search this cost and
+// takes the expert-parallel degree to be small).  With N <= 24 a wave tests
+// at most 2^23 subsets and always finishes; a larger N is refused on the
+// host before anything is enqueued.
+bool assign_ok(const moe_cfg &c) {
+  return c.N <= kMaxAssignNodes && c.R / c.N <= 64;
+}
 
 hipError_t launch_assign(const moe_cfg &c, const int32_t *topk_idx,
                          const int32_t *src_rank, const uint8_t *holds,

@@ -94,7 +94,8 @@ hipError_t launch_sum_nodes(const moe_cfg &c, const void *part, int part_dtype,
                             hipStream_t stream);
 
 // FP8 (E4M3) dispatch with per-block scales (fp8.hip).  Rows are H codes,
-// H/B fp32 scales, zero padding to a multiple of 16 bytes.
+// H/B fp32 scales, zero padding to a multiple of 128 bytes:
+// round_up(H + 4H/B, 128) bytes a row.
 size_t fp8_row_bytes(int H, int B);
 bool fp8_block_ok(const moe_cfg &c, int B);
 
@@ -124,7 +125,8 @@ hipError_t launch_pack_capacity(const moe_cfg &c, const void *x,
 
 // Communication-aware task assignment (assign.hip).
 size_t assign_ws_bytes(const moe_cfg &c);
-bool assign_ok(const moe_cfg &c);  // R/N <= 64 ranks per node
+constexpr int kMaxAssignNodes = 24;  // nodes the cover search accepts
+bool assign_ok(const moe_cfg &c);  // N <= 24 nodes, R/N <= 64 ranks a node
 
 hipError_t launch_assign(const moe_cfg &c, const int32_t *topk_idx,
                          const int32_t *src_rank, const uint8_t *holds,

@@ -392,9 +392,13 @@ int moe_dispatch_combine_capacity(const moe_cfg *cfg, const void *x,
  * give the random and uniform choices of the page).  An expert id outside
  * [0, E), an expert without replica or a source rank outside [0, R) sets
  * the matching MOE_DEVERR_* bit, and that token's ranks are -1.  Needs at
- * most 64 ranks per node (MOE_EUNSUPPORTED otherwise). */
+ * most 24 nodes and at most 64 ranks per node (MOE_EUNSUPPORTED otherwise,
+ * returned on the host before anything is enqueued): the cover search tests
+ * up to 2^(N-1) node subsets per token, the cost the page states, so N is
+ * kept to the small expert-parallel degrees it assumes. */
 
-/* Workspace bytes of moe_assign_tasks (0 when cfg is invalid).  Host only. */
+/* Workspace bytes of moe_assign_tasks (0 when cfg is invalid or N > 24).
+ * Host only. */
 size_t moe_assign_workspace_bytes(const moe_cfg *cfg);
 
 int moe_assign_tasks(const moe_cfg *cfg, const int32_t *topk_idx,

@@ -350,7 +350,7 @@ def fp8_row_bytes(H: int, B: int) -> int:
 def pack_fp8(x: np.ndarray, slot_pos: np.ndarray, B: int = 128) -> np.ndarray:
     """Quantise each token's row once and write it to its K send rows.
 
-    Returns send as uint8 [T*K, round_up(H + 4*H/B, 16)]: H E4M3 codes, then
+    Returns send as uint8 [T*K, round_up(H + 4*H/B, 128)]: H E4M3 codes, then
     H/B fp32 scales, then zero padding, per row.
     """
     x = np.ascontiguousarray(x)

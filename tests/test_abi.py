@@ -196,3 +196,106 @@ def test_assign_entry_point_validates_on_host():
     lib = moe.lib()
     assert lib.moe_assign_tasks(ctypes.byref(c), None, None, None, None, None,
                                 None, None, None, 0, None) == moe.MOE_EINVAL
+
+
+def test_assign_refuses_more_than_24_nodes_on_host():
+    # the cover search tests up to 2^(N-1) node subsets per token ("Cobalt",
+    # Section 3.3): above 24 nodes the call is refused on the host, before
+    # any pointer is looked at or anything is enqueued
+    lib = moe.lib()
+    for N, R, ok in ((24, 48, True), (25, 50, False), (32, 64, False),
+                     (64, 64, False)):
+        c = cfg(E=R * 4, R=R, N=N)
+        assert moe.moe_validate_cfg(c) == moe.MOE_OK
+        ws = lib.moe_assign_workspace_bytes(ctypes.byref(c))
+        rc = lib.moe_assign_tasks(ctypes.byref(c), None, None, None, None,
+                                  None, None, None, None, 0, None)
+        if ok:
+            assert ws > 0
+            assert rc == moe.MOE_EINVAL  # past the node bound: null holds
+        else:
+            assert ws == 0
+            assert rc == moe.MOE_EUNSUPPORTED
+    with pytest.raises(moe.MoeError):
+        moe.alloc_assign_workspace(cfg(E=256, R=64, N=32), device="cpu")
+
+
+def _host(n, dtype):
+    import torch
+    return torch.zeros(n, dtype=dtype)
+
+
+def test_binding_refuses_undersized_buffers_before_any_call():
+    # every wrapper checks each buffer's element count against cfg before
+    # the device check and before the C call; host tensors suffice here
+    import torch
+    c = moe.make_cfg(T=100, H=64, E=16, K=4, R=4, N=2)
+    TK, TH = 400, 100 * 64
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+
+    def refused(fn, name):
+        with pytest.raises(ValueError, match=name):
+            fn()
+
+    refused(lambda: moe.moe_topk_gate(c, _host(100 * 16 - 1, f32),
+                                      _host(TK, i32), _host(TK, f32)),
+            "logits")
+    refused(lambda: moe.moe_topk_gate(c, _host(1600, f32), _host(TK - 1, i32),
+                                      _host(TK, f32)), "topk_idx")
+    refused(lambda: moe.moe_dispatch_pack(c, _host(TH, bf), _host(TK, i32),
+                                          _host(TK * 64 - 8, bf)), "send")
+    refused(lambda: moe.moe_dispatch_pack(c, _host(TH - 64, bf),
+                                          _host(TK, i32), _host(TK * 64, bf)),
+            "x")
+    refused(lambda: moe.moe_combine(c, _host(TK * 64, bf), _host(TK, i32),
+                                    _host(TK, f32), None, None,
+                                    _host(TH - 1, bf)), "out")
+    refused(lambda: moe.moe_combine(c, _host(TK * 64, bf), _host(TK, i32),
+                                    _host(TK, f32), _host(TK, i32),
+                                    _host(15, f32), _host(TH, bf)),
+            "expert_scale")
+    lay = moe.alloc_layout(c, device="cpu")
+    lay.slot_pos = _host(TK - 1, i32)
+    refused(lambda: moe.moe_dispatch_layout(c, _host(TK, i32), lay,
+                                            _host(1 << 16, torch.uint8)),
+            "slot_pos")
+    lay = moe.alloc_layout(c, device="cpu")
+    lay.node_slot = _host(100 * 2 - 1, i32)
+    refused(lambda: moe.moe_dispatch_combine(
+        c, _host(TH, bf), _host(1600, f32), None, _host(TK, i32),
+        _host(TK, f32), lay, _host(TK * 64, bf), _host(TH, bf),
+        _host(1 << 16, torch.uint8)), "node_slot")
+    refused(lambda: moe.moe_dispatch_combine(
+        c, _host(TH, bf), _host(1600, f32), None, _host(TK, i32),
+        _host(TK, f32), moe.alloc_layout(c, device="cpu"),
+        _host(TK * 64 - 1, bf), _host(TH, bf), _host(1 << 16, torch.uint8)),
+        "send")
+    # node-level buffers hold T * min(K, N) rows
+    refused(lambda: moe.moe_dispatch_pack_nodes(
+        c, _host(TH, bf), _host(200, i32), _host(200 * 64 - 1, bf)),
+        "node_send")
+    refused(lambda: moe.moe_combine_nodes(
+        c, _host(200 * 64, f32), _host(200, i32), _host(TH - 1, bf)), "out")
+    # FP8 rows: round_up(H + 4 H / B, 128) bytes each (256 for H = 64)
+    rb = moe.moe_fp8_row_bytes(64, 32)
+    assert rb == 128
+    refused(lambda: moe.moe_dispatch_pack_fp8(
+        c, _host(TH, bf), _host(TK, i32), _host(TK * rb - 1, torch.uint8),
+        qblock=32), "send")
+    # capacity: row_src needs one entry per send row
+    refused(lambda: moe.moe_dispatch_pack_capacity(
+        c, _host(TH, bf), _host(TK, i32), _host(99, i32),
+        torch.zeros((100, 64), dtype=bf)), "row_src")
+    refused(lambda: moe.moe_combine_capacity(
+        c, torch.zeros((100, 63), dtype=bf), _host(TK, i32), _host(TK, f32),
+        None, None, _host(TH, bf)), "y")
+    # assignment
+    refused(lambda: moe.moe_assign_tasks(
+        c, _host(TK, i32), _host(99, i32), torch.zeros(64, dtype=torch.uint8),
+        _host(TK, i32), _host(TK, i32), _host(TK, i32),
+        _host(100, torch.int64), _host(1 << 16, torch.uint8)), "src_rank")
+    # correctly sized host tensors pass the size checks and stop at the
+    # device check, still before the C call
+    with pytest.raises(ValueError, match="device tensor"):
+        moe.moe_dispatch_pack(c, _host(TH, bf), _host(TK, i32),
+                              _host(TK * 64, bf))
