@@ -61,6 +61,9 @@ def _lib() -> ctypes.CDLL:
         lib.moe_ref_combine_partial.argtypes = (
             [ctypes.c_int] * 7 + [_P] * 6 + [ctypes.c_int, ctypes.c_int,
                                             _P, _P])
+        lib.moe_ref_combine_partial_f32.argtypes = (
+            [ctypes.c_int] * 7 + [_P] * 6 + [ctypes.c_int, ctypes.c_int,
+                                            _P, _P])
         lib.moe_ref_combine_nodes.argtypes = (
             [ctypes.c_int] * 4 + [_P, ctypes.c_int, _P, ctypes.c_int, _P,
                                   _P])
@@ -87,7 +90,8 @@ def _lib() -> ctypes.CDLL:
         for f in ("moe_ref_gate", "moe_ref_layout", "moe_ref_pack",
                   "moe_ref_combine", "moe_ref_combine_tokens",
                   "moe_ref_pack_nodes", "moe_ref_forward",
-                  "moe_ref_combine_partial", "moe_ref_combine_nodes"):
+                  "moe_ref_combine_partial", "moe_ref_combine_partial_f32",
+                  "moe_ref_combine_nodes"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -261,12 +265,18 @@ def forward(node_send: np.ndarray, node_slot: np.ndarray,
 def combine_partial(y: np.ndarray, slot_pos: np.ndarray, topk_w: np.ndarray,
                     topk_idx: np.ndarray, expert_scale: Optional[np.ndarray],
                     node_slot: np.ndarray, E: int, R: int,
-                    part_dtype: str = "bf16"):
+                    part_dtype: str = "bf16", accumulate: str = "f64"):
     """Per-node partial sums of each token's weighted expert rows.
 
     Returns ``(part, exact)``: part [D, H] rounded to ``part_dtype`` and the
-    unrounded fp64 sums.
+    unrounded sums.  ``accumulate="f64"`` sums in fp64 (``exact`` is that
+    sum); ``"f32"`` forms the fp32 value a kernel stores before rounding (the
+    fused multiply-add chain over the node's slots in ascending k, see
+    ``moe_ref_combine_partial_f32``), and ``exact`` is that fp32 value.
     """
+    if accumulate == "f32":
+        return _combine_partial_f32(y, slot_pos, topk_w, topk_idx,
+                                    expert_scale, node_slot, E, R, part_dtype)
     y = np.ascontiguousarray(y)
     slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
     topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
@@ -288,6 +298,29 @@ def combine_partial(y: np.ndarray, slot_pos: np.ndarray, topk_w: np.ndarray,
     return part, exact
 
 
+def _combine_partial_f32(y, slot_pos, topk_w, topk_idx, expert_scale,
+                         node_slot, E, R, part_dtype):
+    y = np.ascontiguousarray(y)
+    slot_pos = np.ascontiguousarray(slot_pos, dtype=np.int32)
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    node_slot = np.ascontiguousarray(node_slot, dtype=np.int32)
+    if expert_scale is not None:
+        expert_scale = np.ascontiguousarray(expert_scale, dtype=np.float32)
+    T, K = slot_pos.shape
+    N = node_slot.shape[1]
+    H = y.shape[1]
+    D = node_rows(node_slot)
+    pcode = DT_F32 if part_dtype == "f32" else DT_BF16
+    part = np.zeros((D, H), np.float32 if pcode == DT_F32 else np.uint16)
+    f32 = np.zeros((D, H), np.float32)
+    _check(_lib().moe_ref_combine_partial_f32(
+        T, H, E, K, R, N, _dtype_code(y), _ptr(y), _ptr(slot_pos),
+        _ptr(topk_w), _ptr(topk_idx), _ptr(expert_scale), _ptr(node_slot), D,
+        pcode, _ptr(part), _ptr(f32)), "combine_partial_f32")
+    return part, f32.astype(np.float64)
+
+
 def combine_nodes(part: np.ndarray, node_slot: np.ndarray,
                   out_dtype: str = "bf16"):
     """Sum of each token's node partials: ``(out, exact)`` as in combine."""
@@ -307,9 +340,11 @@ def combine_nodes(part: np.ndarray, node_slot: np.ndarray,
 def dispatch_combine_nodes(x: np.ndarray, logits: np.ndarray, K: int, R: int,
                            N: int, expert_scale: Optional[np.ndarray] = None,
                            out_dtype: str = "bf16", part_dtype: str = "bf16",
-                           renorm: bool = True) -> dict:
+                           renorm: bool = True,
+                           accumulate: str = "f64") -> dict:
     """The two-leg path: gate -> layout -> leg 1 -> leg 2 -> per-node
-    partials (Y = send) -> sum at the source."""
+    partials (Y = send; summed as ``accumulate`` says, see
+    ``combine_partial``) -> sum of the stored partials at the source."""
     idx, w = gate(logits, K, renorm)
     E = logits.shape[1]
     lay = layout(idx, E, R, N)
@@ -317,7 +352,7 @@ def dispatch_combine_nodes(x: np.ndarray, logits: np.ndarray, K: int, R: int,
     send = forward(node_send, lay["node_slot"], idx, lay["slot_pos"], E, R)
     part, part_exact = combine_partial(send, lay["slot_pos"], w, idx,
                                        expert_scale, lay["node_slot"], E, R,
-                                       part_dtype)
+                                       part_dtype, accumulate)
     out, out_exact = combine_nodes(part, lay["node_slot"], out_dtype)
     res = dict(lay)
     res.update(topk_idx=idx, topk_w=w, node_send=node_send, send=send,

@@ -7,7 +7,10 @@
  * the benchmark's CPU-baseline leg may build, load or call it.  It shares no
  * code, header, table or helper with the HIP library, and includes nothing
  * from it.  Floating point that produces a value is done in fp64; fp32 is used
- * only where the inputs are fp32 (the logit comparisons that choose experts).
+ * only where the inputs are fp32 (the logit comparisons that choose experts),
+ * where a value is an integer decision taken in fp32 (FP8 codes), and in the
+ * one function that states the fp32 value a stored 16-bit partial sum is
+ * rounded from (moe_ref_combine_partial_f32).
  *
  * Sources (page title, section):
  *  - "Efficient and portable mixture-of-experts communication", "Introdución":
@@ -450,6 +453,53 @@ int moe_ref_combine_partial(int T, int H, int E, int K, int R, int N,
         size_t o = (size_t)p * H + h;
         if (part_exact) part_exact[o] = acc;
         if (part) store_value(part_dtype, part, o, acc);
+      }
+    }
+  }
+  return REF_OK;
+}
+
+/* The same partials as the fp32 value a kernel stores before its one
+ * rounding to part_dtype.  Reading of "the fp32 sum of the token's weighted
+ * expert outputs on that node" ("MoX: Efficient MoE Routing on
+ * Direct-Connect Topologies", Section 2.5: a node reduces the expert outputs
+ * it holds before forwarding one vector): the coefficient is the fp32
+ * product c = w[t,k] * s[e(t,k)], and the sum is the chain acc <- fma(c,
+ * y, acc) from acc = +0 over the node's slots in ascending k, every step
+ * rounded once to fp32.  It fixes which fp32 value a 16-bit partial is
+ * rounded from, so both sides take that rounding decision in the same
+ * precision.  Slots with slot_pos < 0 add nothing.  part_f32 (may be NULL)
+ * gets the fp32 sums, part (may be NULL) those sums rounded to nearest-even
+ * in part_dtype. */
+int moe_ref_combine_partial_f32(int T, int H, int E, int K, int R, int N,
+                                int y_dtype, const void *y,
+                                const int32_t *slot_pos, const float *topk_w,
+                                const int32_t *topk_idx,
+                                const float *expert_scale,
+                                const int32_t *node_slot, int D,
+                                int part_dtype, void *part, float *part_f32) {
+  if (T < 0 || H < 1 || E < 1 || K < 1 || R < 1 || N < 1) return REF_EINVAL;
+  if (E % R != 0 || R % N != 0) return REF_EINVAL;
+  const int per_rank = E / R, per_node = R / N;
+  for (int t = 0; t < T; ++t) {
+    for (int n = 0; n < N; ++n) {
+      int32_t p = node_slot[(size_t)t * N + n];
+      if (p < 0) continue;
+      if (p >= D) return REF_EINVAL;
+      for (int h = 0; h < H; ++h) {
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {
+          size_t i = (size_t)t * K + k;
+          int e = topk_idx[i];
+          if ((e / per_rank) / per_node != n || slot_pos[i] < 0) continue;
+          float c = topk_w[i];
+          if (expert_scale) c = c * expert_scale[e];
+          float v = (float)row_value(y_dtype, y, (size_t)slot_pos[i] * H + h);
+          acc = fmaf(c, v, acc);
+        }
+        size_t o = (size_t)p * H + h;
+        if (part_f32) part_f32[o] = acc;
+        if (part) store_value(part_dtype, part, o, (double)acc);
       }
     }
   }

@@ -10,6 +10,7 @@ import torch
 
 import combine_moe_topk_amd as moe
 import moe_inputs as mi
+import oracle
 
 # Combine tolerances (stated for the combine in the target of this work):
 # fp32 outputs within 1e-5 relative to sum_k |w_k s_k y_k|, bf16 outputs
@@ -147,3 +148,38 @@ def rows_f64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return mi.bf16_bits_to_f32(a).astype(np.float64)
     return a.astype(np.float64)
+
+
+def abs_rows(a: np.ndarray) -> np.ndarray:
+    """|a| for fp32 rows or bf16 bit patterns (sign bit cleared)."""
+    return (a & np.uint16(0x7FFF)) if a.dtype == np.uint16 else np.abs(a)
+
+
+def check_all_tokens(out: np.ndarray, T: int, exact_of, abs_of, odt: str,
+                     chunk: int = 2048) -> None:
+    """Every output token against the oracle, a chunk of tokens at a time.
+
+    exact_of(toks) gives the oracle's unrounded fp64 rows of those tokens;
+    abs_of(toks) the same sum over |terms| (the fp32 error scale; only
+    called for fp32 outputs)."""
+    for lo in range(0, T, chunk):
+        toks = np.arange(lo, min(T, lo + chunk), dtype=np.int32)
+        sc = abs_of(toks) if odt == mi.F32 else None
+        check_out(out[lo:lo + len(toks)], exact_of(toks), sc, odt)
+
+
+def check_combine_all(out: np.ndarray, y: np.ndarray, slot_pos: np.ndarray,
+                      topk_w: np.ndarray, topk_idx, scale, odt: str,
+                      chunk: int = 2048) -> None:
+    """Every token of a combine over rows y against oracle.combine_tokens
+    (slots < 0 add nothing; weights and scales are non-negative)."""
+    ay = abs_rows(y) if odt == mi.F32 else None
+    check_all_tokens(
+        out, slot_pos.shape[0],
+        lambda toks: oracle.combine_tokens(toks, y, slot_pos, topk_w,
+                                           topk_idx, scale),
+        lambda toks: oracle.combine_tokens(toks, ay, slot_pos,
+                                           np.abs(topk_w), topk_idx,
+                                           None if scale is None
+                                           else np.abs(scale)),
+        odt, chunk)

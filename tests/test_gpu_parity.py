@@ -15,9 +15,10 @@ import torch
 import combine_moe_topk_amd as moe
 import moe_inputs as mi
 import oracle
-from helpers import (ATOL_BF16, LAYOUT_KEYS, cfg_of, check_gate, check_layout,
-                     check_out, dev, host, layout_to_host, out_dtype,
-                     require_gpu, row_dtype, rows_f64, run_fused, term_scale)
+from helpers import (ATOL_BF16, LAYOUT_KEYS, cfg_of, check_combine_all,
+                     check_gate, check_layout, check_out, dev, host,
+                     layout_to_host, out_dtype, require_gpu, row_dtype,
+                     rows_f64, run_fused, term_scale)
 
 pytestmark = pytest.mark.gpu
 
@@ -280,20 +281,37 @@ def test_combine_burst_ragged(odt):
     moe.moe_combine(cfg_of(w), dev(y), dev(slot_pos), dev(wt), dev(idx),
                     dev(scale), out)
     got = host(out)
-    ref_out, exact = oracle.combine(y, slot_pos, wt, idx, scale, odt)
+    # every token, fp32 outputs against sum |terms| as well
+    check_combine_all(got, y, slot_pos, wt, idx, scale, odt)
     if odt == mi.BF16:
-        check_out(got, exact, None, odt)
+        ref_out, _ = oracle.combine(y, slot_pos, wt, idx, scale, odt)
         assert np.mean(got == ref_out) > 0.99
-    else:
-        toks = np.unique(np.concatenate(
-            [np.arange(16), np.arange(w.T - 3, w.T),
-             rng.integers(0, w.T, 256)]))
-        coef = np.where(drop, 0.0, wt.astype(np.float64) * scale[idx])
-        sp = np.where(drop, 0, slot_pos)[toks]
-        ysel = rows_f64(y[sp.ravel()]).reshape(len(toks), w.K, w.H)
-        bound = np.einsum("tk,tkh->th", np.abs(coef[toks]), np.abs(ysel))
-        check_out(got[toks], exact[toks], bound, odt)
     assert not got[-1].any()
+
+
+# The fp32-row burst kernels (8 fp32 elements a thread take two 16-byte
+# loads; K = 8 and K = 4 keep 8 row loads in flight): 1 GiB or more of fp32
+# y rows, every token compared, both output types.
+@pytest.mark.parametrize("K", [8, 4])
+@pytest.mark.parametrize("odt", [mi.BF16, mi.F32])
+def test_combine_burst_f32_rows(odt, K):
+    T = 9000 if K == 8 else 18000
+    w = mi.Workload("burst_f32", T=T, H=4096, E=64, K=K, R=16, N=4,
+                    x_dtype=mi.F32, out_dtype=odt)
+    assert w.T * w.K * w.H * 4 >= 1 << 30
+    idx = mi.random_topk_idx(w.T, w.E, w.K, seed=11)
+    rng = np.random.Generator(np.random.PCG64(11))
+    wt = rng.random((w.T, w.K), dtype=np.float32) + np.float32(0.1)
+    wt = (wt / wt.sum(axis=1, keepdims=True)).astype(np.float32)
+    scale = (1.0 + 0.01 * (np.arange(w.E) % 8)).astype(np.float32)
+    slot_pos = oracle.layout(idx, w.E, w.R, w.N)["slot_pos"]
+    # 1.2 GB of fp32 rows drawn from 4096 distinct seeded rows
+    y = mi.random_x(4096, w.H, mi.F32, seed=12)[
+        rng.integers(0, 4096, w.T * w.K)]
+    out = torch.empty((w.T, w.H), dtype=out_dtype(w), device="cuda")
+    moe.moe_combine(cfg_of(w), dev(y), dev(slot_pos), dev(wt), dev(idx),
+                    dev(scale), out)
+    check_combine_all(host(out), y, slot_pos, wt, idx, scale, odt)
 
 
 # ---------------------------------------------------------------- fused ----
@@ -336,21 +354,11 @@ def test_fused_full_size(w, seed):
     for lo in range(0, w.T * w.K, 1 << 16):
         hi = min(lo + (1 << 16), w.T * w.K)
         assert torch.equal(send[lo:hi], x[src_tok[lo:hi]]), (lo, hi)
-    # sampled tokens: oracle's own pack and fp64 combine
+    # every token: the oracle's own pack, then its fp64 combine of the
+    # packed rows, a chunk of tokens at a time
     ref_send = oracle.pack(d["x"], lay["slot_pos"])
-    rng = np.random.Generator(np.random.PCG64(5))
-    toks = np.unique(np.concatenate([[0, w.T - 1],
-                                     rng.integers(0, w.T, 254)])).astype(np.int32)
-    rows = lay["slot_pos"][toks].ravel()
-    np.testing.assert_array_equal(host(send[torch.from_numpy(rows).long().cuda()]),
-                                  ref_send[rows])
-    exact = oracle.combine_tokens(toks, ref_send, lay["slot_pos"], wt, idx,
-                                  d["expert_scale"])
-    coef = wt.astype(np.float64) * (1.0 if d["expert_scale"] is None
-                                    else d["expert_scale"][idx])
-    check_out(res["out"][toks], exact,
-              term_scale(rows_f64(ref_send), lay["slot_pos"], coef, toks),
-              w.out_dtype)
+    check_combine_all(res["out"], ref_send, lay["slot_pos"], wt, idx,
+                      d["expert_scale"], w.out_dtype)
 
 
 # ----------------------------------------------------------- edge cases ----
@@ -485,3 +493,40 @@ def test_host_errors_enqueue_nothing():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_dispatch_pack(cfg, x, sp, send[1:])  # 2-byte aligned
     assert ei.value.code == moe.MOE_EUNSUPPORTED
+
+
+def test_undersized_buffers_refused_before_enqueue():
+    # the binding checks every buffer against cfg before the C call: an
+    # undersized tensor raises ValueError and no kernel touches any output
+    w = mi.DEEPSEEK_V3.replace(T=64, H=64)
+    cfg = cfg_of(w)
+    T, K, H = w.T, w.K, w.H
+    d = mi.make_inputs(w)
+    x, lg = dev(d["x"]), dev(d["logits"])
+    idx = torch.full((T * K,), -5, dtype=torch.int32, device="cuda")
+    wt = torch.full((T * K,), -5.0, dtype=torch.float32, device="cuda")
+    lay = moe.alloc_layout(cfg)
+    lay.slot_pos.fill_(-5)
+    send = torch.full((T * K, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((T, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    ws = moe.alloc_workspace(cfg)
+    torch.cuda.synchronize()
+    short = {"send": send[:-1], "out": out[:-1], "x": x[:-1],
+             "logits": lg[:-1], "topk_idx": idx[:-1], "topk_w": wt[:-1]}
+    for name, t in short.items():
+        args = dict(x=x, logits=lg, topk_idx=idx, topk_w=wt, send=send,
+                    out=out)
+        args[name] = t
+        with pytest.raises(ValueError, match=name):
+            moe.moe_dispatch_combine(cfg, args["x"], args["logits"], None,
+                                     args["topk_idx"], args["topk_w"], lay,
+                                     args["send"], args["out"], ws)
+    lay.node_slot = lay.node_slot[:-1]
+    with pytest.raises(ValueError, match="node_slot"):
+        moe.moe_dispatch_combine(cfg, x, lg, None, idx, wt, lay, send, out, ws)
+    with pytest.raises(ValueError, match="^y:"):
+        moe.moe_combine(cfg, send[:-1], lay.slot_pos, wt, idx, None, out)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and bool((send == 3.0).all())
+    assert bool((idx == -5).all()) and bool((wt == -5.0).all())
+    assert bool((lay.slot_pos == -5).all())

@@ -187,6 +187,101 @@ def test_partial_rounding(pdt):
             part, oracle.f64_to_bf16(pex).reshape(part.shape))
 
 
+# ------------------------------------------- fp32 partials as stored ----
+# The fp32 value a stored partial is rounded from: c = fp32(w * s), then
+# acc <- fma(c, y, acc) from +0 over the node's slots in ascending k, each
+# step rounded once to fp32.  Pinned by exact rational arithmetic with a
+# brute-force nearest-fp32 rounding, by a case where the slot order decides
+# the result, and by the fp32 error bound around the fp64 partial.
+
+def _round_f32(q):
+    """Nearest fp32 to the rational q, ties to the even significand, found
+    by comparing the exact distances of three neighbouring candidates."""
+    from fractions import Fraction
+    if q == 0:
+        return np.float32(0.0)
+    c = np.float32(float(q))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c,
+             np.nextafter(c, np.float32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - q),
+                                     int(np.array(v).view(np.uint32)) & 1))
+
+
+@pytest.mark.parametrize("ydt", [mi.F32, mi.BF16])
+def test_partial_f32_chain_exact_fractions(ydt):
+    from fractions import Fraction
+    w = mi.Workload("chain", T=7, H=3, E=8, K=5, R=4, N=2, x_dtype=ydt,
+                    out_dtype=mi.F32, expert="mod8")
+    d, idx, wt, lay = _route(w)
+    rng = np.random.Generator(np.random.PCG64(21))
+    y = mi.random_x(w.T * w.K, w.H, ydt, seed=21)
+    yv = mi.bf16_bits_to_f32(y) if ydt == mi.BF16 else y
+    s = d["expert_scale"]
+    wt = (wt * np.float32(3.0) * rng.random(wt.shape, dtype=np.float32))
+    part, f32 = oracle.combine_partial(y, lay["slot_pos"], wt, idx, s,
+                                       lay["node_slot"], w.E, w.R, "bf16",
+                                       accumulate="f32")
+    per_node = (w.E // w.R) * (w.R // w.N)
+    for t in range(w.T):
+        for n in range(w.N):
+            p = lay["node_slot"][t, n]
+            if p < 0:
+                continue
+            for h in range(w.H):
+                acc = np.float32(0.0)
+                for k in range(w.K):
+                    e = idx[t, k]
+                    if e // per_node != n:
+                        continue
+                    c = _round_f32(Fraction(float(wt[t, k])) *
+                                   Fraction(float(s[e])))
+                    v = Fraction(float(yv[lay["slot_pos"][t, k], h]))
+                    acc = _round_f32(Fraction(float(c)) * v +
+                                     Fraction(float(acc)))
+                assert f32[p, h] == acc, (t, n, h)
+    # the stored bf16 partial is that fp32 value rounded once
+    np.testing.assert_array_equal(part,
+                                  oracle.f64_to_bf16(f32).reshape(part.shape))
+
+
+def test_partial_f32_chain_takes_slots_in_ascending_order():
+    # one token, three slots on node 0 with rows 1, 2^27, -2^27 (weights 1):
+    # ascending k gives fma chain 1 -> 2^27 (2^27 + 1 rounds down) -> 0,
+    # while the fp64 partial is 1 and descending order would give 1
+    y = np.zeros((3, 8), np.float32)
+    y[0], y[1], y[2] = 1.0, 2.0 ** 27, -(2.0 ** 27)
+    idx = np.array([[0, 1, 2]], np.int32)
+    sp = np.array([[0, 1, 2]], np.int32)
+    wt = np.ones((1, 3), np.float32)
+    ns = np.array([[0, -1]], np.int32)
+    # E = 6 experts on R = 2 ranks, N = 2 nodes: experts 0-2 on node 0
+    _, f32 = oracle.combine_partial(y, sp, wt, idx, None, ns, 6, 2, "f32",
+                                    accumulate="f32")
+    _, f64 = oracle.combine_partial(y, sp, wt, idx, None, ns, 6, 2, "f32")
+    assert np.all(f32 == 0.0) and np.all(f64 == 1.0)
+
+
+@pytest.mark.parametrize("w", SHAPES, ids=lambda w: w.name)
+def test_partial_f32_chain_within_fp32_error(w):
+    d, idx, wt, lay = _route(w)
+    send = oracle.pack(d["x"], lay["slot_pos"])
+    _, f32 = oracle.combine_partial(send, lay["slot_pos"], wt, idx,
+                                    d["expert_scale"], lay["node_slot"], w.E,
+                                    w.R, "f32", accumulate="f32")
+    _, f64 = oracle.combine_partial(send, lay["slot_pos"], wt, idx,
+                                    d["expert_scale"], lay["node_slot"], w.E,
+                                    w.R, "f32")
+    ab = (send & np.uint16(0x7FFF)) if send.dtype == np.uint16 else np.abs(send)
+    _, sc = oracle.combine_partial(ab, lay["slot_pos"], wt, idx,
+                                   d["expert_scale"], lay["node_slot"], w.E,
+                                   w.R, "f32")
+    # K fma roundings and one coefficient rounding, each within 2^-24 of
+    # the running magnitude, which is at most sum |terms|
+    bound = (w.K + 1) * 2.0 ** -24 * sc
+    assert np.all(np.abs(f32 - f64) <= bound + 1e-300)
+    assert np.any(f32 != f64)  # not the fp64 sum in disguise
+
+
 # --------------------------------------------------------- sum of nodes ----
 
 @pytest.mark.parametrize("w", SHAPES, ids=lambda w: w.name)
