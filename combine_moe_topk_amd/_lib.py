@@ -21,6 +21,8 @@ MOE_EINVAL = -1
 MOE_EUNSUPPORTED = -2
 MOE_EWORKSPACE = -3
 MOE_ELAUNCH = -4
+MOE_ESCRATCH = -5
+MOE_SCRATCH_BYTES = 1 << 20
 
 MOE_DEVERR_EXPERT_RANGE = 0x1
 MOE_DEVERR_DUP_EXPERT = 0x2
@@ -99,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P,
                                                     _LAY, _P, _P, _P,
                                                     ctypes.c_size_t, _P]),
+            "moe_dispatch_combine_noalloc": (ctypes.c_int, [
+                _CFG, _P, _P, _P, _P, _P, _LAY, _P, _P, _P]),
             "moe_node_rows_max": (ctypes.c_size_t, [_CFG]),
             "moe_dispatch_pack_nodes": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
             "moe_dispatch_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P,
@@ -395,6 +399,29 @@ def moe_dispatch_combine(cfg: moe_cfg, x: torch.Tensor, logits: torch.Tensor,
         _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"),
         _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
         "moe_dispatch_combine")
+
+
+def moe_dispatch_combine_noalloc(cfg: moe_cfg, x: torch.Tensor,
+                                 logits: torch.Tensor,
+                                 expert_scale: Optional[torch.Tensor],
+                                 topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                                 layout: Layout, send: torch.Tensor,
+                                 out: torch.Tensor, stream=None) -> None:
+    """moe_dispatch_combine with the layout workspace in the library's
+    static device scratch (MOE_SCRATCH_BYTES): nothing is allocated."""
+    _need_front(cfg, x, logits, expert_scale, topk_idx, topk_w)
+    _need(send, cfg.T * cfg.K * cfg.H, "send")
+    _need(out, cfg.T * cfg.H, "out")
+    lay = layout.c_struct(cfg)
+    _check(lib().moe_dispatch_combine_noalloc(
+        ctypes.byref(cfg), _ptr(x, _row_dtype(cfg), "x"),
+        _ptr(logits, torch.float32, "logits"),
+        _ptr(expert_scale, torch.float32, "expert_scale"),
+        _ptr(topk_idx, torch.int32, "topk_idx"),
+        _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(lay),
+        _ptr(send, _row_dtype(cfg), "send"),
+        _ptr(out, TORCH_DTYPE[cfg.out_dtype], "out"), _stream(stream)),
+        "moe_dispatch_combine_noalloc")
 
 
 # ---- node-level two-leg dispatch and hierarchical combine -----------------

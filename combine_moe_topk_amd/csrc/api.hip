@@ -66,6 +66,35 @@ __global__ void fill_u32_kernel(uint32_t *p, uint32_t v, size_t n) {
 }  // namespace
 
 namespace moe {
+
+int check_fused(const moe_cfg *cfg, const void *x, const float *logits,
+                const int32_t *topk_idx, const float *topk_w,
+                const moe_layout *layout, const void *send, const void *out) {
+  int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_layout_ptrs(cfg, layout)) != MOE_OK) return rc;
+  if (cfg->T > 0) {
+    if (!x || !logits || !topk_idx || !topk_w || !send || !out)
+      return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(send) || !aligned16(out))
+      return MOE_EUNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+hipError_t launch_fused(const moe_cfg &c, const void *x, const float *logits,
+                        const float *expert_scale, int32_t *topk_idx,
+                        float *topk_w, const moe_layout &lay, void *send,
+                        void *out, void *ws, hipStream_t stream) {
+  hipError_t e = launch_gate(c, logits, topk_idx, topk_w, stream);
+  if (e == hipSuccess) e = launch_layout(c, topk_idx, lay, ws, stream);
+  if (e == hipSuccess) e = launch_pack(c, x, lay.slot_pos, send, stream);
+  if (e == hipSuccess)
+    e = launch_combine(c, send, lay.slot_pos, topk_w, topk_idx, expert_scale,
+                       out, stream);
+  return e;
+}
+
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t n,
                            hipStream_t stream) {
   if (n == 0) return hipSuccess;
@@ -143,23 +172,13 @@ int moe_dispatch_combine(const moe_cfg *cfg, const void *x,
                          int32_t *topk_idx, float *topk_w,
                          const moe_layout *layout, void *send, void *out,
                          void *ws, size_t ws_bytes, hipStream_t stream) {
-  int rc = validate(cfg);
+  int rc = moe::check_fused(cfg, x, logits, topk_idx, topk_w, layout, send,
+                            out);
   if (rc != MOE_OK) return rc;
-  if ((rc = check_layout_ptrs(cfg, layout)) != MOE_OK) return rc;
   if ((rc = check_ws(cfg, ws, ws_bytes)) != MOE_OK) return rc;
-  if (cfg->T > 0) {
-    if (!x || !logits || !topk_idx || !topk_w || !send || !out)
-      return MOE_EINVAL;
-    if (!aligned16(x) || !aligned16(send) || !aligned16(out))
-      return MOE_EUNSUPPORTED;
-  }
-  hipError_t e = moe::launch_gate(*cfg, logits, topk_idx, topk_w, stream);
-  if (e == hipSuccess) e = moe::launch_layout(*cfg, topk_idx, *layout, ws, stream);
-  if (e == hipSuccess) e = moe::launch_pack(*cfg, x, layout->slot_pos, send, stream);
-  if (e == hipSuccess)
-    e = moe::launch_combine(*cfg, send, layout->slot_pos, topk_w, topk_idx,
-                            expert_scale, out, stream);
-  return launch_status(e);
+  return launch_status(moe::launch_fused(*cfg, x, logits, expert_scale,
+                                         topk_idx, topk_w, *layout, send, out,
+                                         ws, stream));
 }
 
 size_t moe_node_rows_max(const moe_cfg *cfg) {
@@ -470,6 +489,8 @@ const char *moe_strerror(int code) {
     case MOE_EUNSUPPORTED: return "unsupported dtype, alignment or size";
     case MOE_EWORKSPACE: return "workspace missing or too small";
     case MOE_ELAUNCH: return "HIP launch or copy failed";
+    case MOE_ESCRATCH:
+      return "workspace larger than the library's static scratch (1 MiB)";
     default: return "unknown error code";
   }
 }

@@ -48,6 +48,17 @@ LayoutGeom layout_geom(const moe_cfg &c);
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, size_t n,
                            hipStream_t stream);
 
+// The fused call's host checks (cfg, layout and row pointers; not the
+// workspace) and its launch sequence gate -> layout -> pack -> combine, the
+// combine reading send.  ws holds layout_geom(c).ws_bytes.
+int check_fused(const moe_cfg *cfg, const void *x, const float *logits,
+                const int32_t *topk_idx, const float *topk_w,
+                const moe_layout *layout, const void *send, const void *out);
+hipError_t launch_fused(const moe_cfg &c, const void *x, const float *logits,
+                        const float *expert_scale, int32_t *topk_idx,
+                        float *topk_w, const moe_layout &lay, void *send,
+                        void *out, void *ws, hipStream_t stream);
+
 hipError_t launch_gate(const moe_cfg &c, const float *logits,
                        int32_t *topk_idx, float *topk_w, hipStream_t stream);
 

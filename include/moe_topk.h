@@ -60,6 +60,7 @@ extern "C" {
 #define MOE_EUNSUPPORTED (-2) /* valid but not supported: dtype, alignment   */
 #define MOE_EWORKSPACE (-3)   /* workspace missing or smaller than required  */
 #define MOE_ELAUNCH (-4)      /* a HIP launch or copy reported an error      */
+#define MOE_ESCRATCH (-5)     /* needs more than the library's static scratch */
 
 /* ---- device-detected input errors (bits of the workspace error word) --- */
 #define MOE_DEVERR_EXPERT_RANGE 0x1 /* a topk_idx entry outside [0, E)      */
@@ -196,6 +197,29 @@ int moe_dispatch_combine(const moe_cfg *cfg, const void *x,
                          int32_t *topk_idx, float *topk_w,
                          const moe_layout *layout, void *send, void *out,
                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_dispatch_combine without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The layout's workspace
+ * (error word and per-tile count table, moe_workspace_bytes(cfg) bytes) is
+ * kept in a static device array of MOE_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * nothing.  The caller passes every input and output, as above, and gets the
+ * same results.  Returns MOE_ESCRATCH, before anything is enqueued, when
+ * moe_workspace_bytes(cfg) exceeds MOE_SCRATCH_BYTES (1 MiB, with the
+ * default layout tile: up to 204288 tokens at E = 256, R = 64, N = 8;
+ * 64256 at E = 896, R = 128, N = 16; 3904 at E = 4096).
+ * `stream` must belong to the current device.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race, so the caller orders them.  The array's error word is
+ * cleared at the start of each call; the expert ids come from the call's
+ * own gate, so no device-detected error arises. */
+#define MOE_SCRATCH_BYTES (1u << 20)
+int moe_dispatch_combine_noalloc(const moe_cfg *cfg, const void *x,
+                                 const float *logits,
+                                 const float *expert_scale, int32_t *topk_idx,
+                                 float *topk_w, const moe_layout *layout,
+                                 void *send, void *out, hipStream_t stream);
 
 /* ---- node-level two-leg dispatch and hierarchical combine -------------
  * "Cobalt: Leveraging Expert Co-activation for Efficient Distributed MoE
