@@ -87,7 +87,12 @@ hipError_t launch_fused(const moe_cfg &c, const void *x, const float *logits,
                         float *topk_w, const moe_layout &lay, void *send,
                         void *out, void *ws, hipStream_t stream) {
   hipError_t e = launch_gate(c, logits, topk_idx, topk_w, stream);
-  if (e == hipSuccess) e = launch_layout(c, topk_idx, lay, ws, stream);
+  if (e != hipSuccess) return e;
+  // a decode-sized batch: layout, pack and combine in one launch
+  if (decode_ok(c) && aligned16(topk_idx))
+    return launch_decode(c, x, topk_idx, topk_w, expert_scale, lay, send, out,
+                         stream);
+  e = launch_layout(c, topk_idx, lay, ws, stream);
   if (e == hipSuccess) e = launch_pack(c, x, lay.slot_pos, send, stream);
   if (e == hipSuccess)
     e = launch_combine(c, send, lay.slot_pos, topk_w, topk_idx, expert_scale,

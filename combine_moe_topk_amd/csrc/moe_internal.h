@@ -81,6 +81,16 @@ hipError_t launch_combine(const moe_cfg &c, const void *y,
                           const int32_t *topk_idx, const float *expert_scale,
                           void *out, hipStream_t stream, int rows = -1);
 
+// Decode-sized fused step (decode.hip): layout, pack and combine of a small
+// batch in one launch after the gate, the same results as the layout, pack
+// and combine kernels.  decode_ok: the batch fits (1 <= T <= 1024, T*K <=
+// 4096, its LDS tables within 64 KiB).
+bool decode_ok(const moe_cfg &c);
+hipError_t launch_decode(const moe_cfg &c, const void *x,
+                         const int32_t *topk_idx, const float *topk_w,
+                         const float *expert_scale, const moe_layout &lay,
+                         void *send, void *out, hipStream_t stream);
+
 // Node-level two-leg dispatch and hierarchical combine (nodes.hip).  Leg-1
 // and partial buffers hold node_rows_max(c) = T * min(K, N) rows.
 int node_rows_max(const moe_cfg &c);

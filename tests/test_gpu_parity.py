@@ -405,6 +405,66 @@ def test_fused_edge_shapes(T, H, E, K, R, N, xdt, odt):
               term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef), odt)
 
 
+# Batches of up to 1024 tokens (T*K <= 4096) take the one-launch decode
+# step after the gate: ragged and tiny batches, K = 1 and K = E, many nodes,
+# E = 1024, fp32 rows and outputs, no expert scale, no optional outputs.
+DECODE_SHAPES = [
+    # T, H, E, K, R, N, xdt, odt, expert, optional
+    (1, 64, 8, 1, 8, 1, mi.BF16, mi.BF16, "mod8", True),
+    (37, 7168, 256, 8, 64, 8, mi.BF16, mi.BF16, "mod8", True),
+    (128, 7168, 256, 8, 64, 8, mi.BF16, mi.F32, "identity", False),
+    (77, 520, 64, 32, 64, 64, mi.F32, mi.BF16, "mod8", True),   # K = 32
+    (255, 1000, 1024, 16, 128, 16, mi.BF16, mi.BF16, "mod8", True),
+    (512, 256, 128, 8, 64, 8, mi.F32, mi.F32, "mod8", True),
+    (1024, 128, 32, 4, 8, 2, mi.BF16, mi.BF16, "mod8", False),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES,
+                         ids=lambda c: f"T{c[0]}-H{c[1]}-E{c[2]}-K{c[3]}")
+def test_fused_decode_path(case):
+    T, H, E, K, R, N, xdt, odt, expert, optional = case
+    w = mi.Workload("decode", T=T, H=H, E=E, K=K, R=R, N=N, x_dtype=xdt,
+                    out_dtype=odt, expert=expert)
+    d = mi.make_inputs(w)
+    ref = oracle.dispatch_combine(d["x"], d["logits"], K, R, N,
+                                  d["expert_scale"], odt)
+    cfg = cfg_of(w)
+    x, lg = dev(d["x"]), dev(d["logits"])
+    sc = None if d["expert_scale"] is None else dev(d["expert_scale"])
+    idx = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T * K, dtype=torch.float32, device="cuda")
+    lay = moe.alloc_layout(cfg, optional=optional)
+    send = torch.empty((T * K, H), dtype=row_dtype(w), device="cuda")
+    out = torch.empty((T, H), dtype=out_dtype(w), device="cuda")
+    ws = moe.alloc_workspace(cfg)
+    moe.moe_dispatch_combine(cfg, x, lg, sc, idx, wt, lay, send, out, ws)
+    assert moe.moe_read_device_error(ws) == 0
+    res = layout_to_host(lay, T, K, N)
+    res.update(topk_idx=host(idx).reshape(T, K), topk_w=host(wt).reshape(T, K))
+    check_gate(res, ref["topk_idx"], ref["topk_w"])
+    check_layout(res, ref)
+    np.testing.assert_array_equal(host(send), ref["send"])
+    coef = ref["topk_w"].astype(np.float64)
+    if d["expert_scale"] is not None:
+        coef = coef * d["expert_scale"][ref["topk_idx"]]
+    check_out(host(out), ref["out_exact"],
+              term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef), odt)
+    # the same bits as the layout, pack and combine calls one by one
+    ws2 = moe.alloc_workspace(cfg)
+    lay2 = moe.alloc_layout(cfg, optional=optional)
+    send2 = torch.empty_like(send)
+    out2 = torch.empty_like(out)
+    moe.moe_dispatch_layout(cfg, idx, lay2, ws2)
+    moe.moe_dispatch_pack(cfg, x, lay2.slot_pos, send2)
+    moe.moe_combine(cfg, send2, lay2.slot_pos, wt, idx, sc, out2)
+    for name in LAYOUT_KEYS:
+        a, b = getattr(lay, name), getattr(lay2, name)
+        if a is not None:
+            assert torch.equal(a, b), name
+    assert torch.equal(send, send2) and torch.equal(out, out2)
+
+
 def test_identity_experts_return_input():
     # renormalised weights and identity experts: out == x (bf16), the dispatch
     # permutation inverting exactly under the combine
