@@ -166,6 +166,17 @@ def load_traffic(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+def traffic_source(kernel: str, workload: str, traffic) -> str:
+    """Where roofline.traffic comes from: it is not measured in this run."""
+    if traffic is None:
+        return ("none: no committed counters for this kernel and workload, "
+                "or its source changed since they were taken")
+    return (f"profiles/traffic.json entry {kernel}/{workload}: rocprofv3 "
+            f"FETCH_SIZE + WRITE_SIZE per launch from committed runs, "
+            f"scaled by a plain copy's reading; kernel source sha "
+            f"{source_digest(KERNEL_SOURCES[kernel])} unchanged since")
+
+
 def load_valu(workload: str):
     """Vector instructions one moe_assign_tasks call issues, from committed
     rocprofv3 counters; null when absent or the source changed since."""
@@ -187,10 +198,16 @@ def cpu_baseline(w: mi.Workload, d: dict, sample_tokens: int) -> dict:
     x = np.ascontiguousarray(d["x"][:Ts])
     lg = np.ascontiguousarray(d["logits"][:Ts])
     oracle.gate(lg[:2], w.K)  # load the library outside the timing
-    t0 = time.perf_counter()
-    oracle.dispatch_combine(x, lg, w.K, w.R, w.N, d["expert_scale"],
-                            w.out_dtype)
-    dt = time.perf_counter() - t0
+    # whole passes of the oracle over the sample until about 10 s of CPU
+    # work (at most 8 passes); throughput over all passes
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.dispatch_combine(x, lg, w.K, w.R, w.N, d["expert_scale"],
+                                w.out_dtype)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or reps >= 8:
+            break
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -198,15 +215,166 @@ def cpu_baseline(w: mi.Workload, d: dict, sample_tokens: int) -> dict:
                         if ln.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": Ts / dt, "unit": "tokens/s", "cores": 1,
+    return {"value": reps * Ts / dt, "unit": "tokens/s", "cores": 1,
             "kind": "oracle", "cpu": cpu, "host_cpus": os.cpu_count(),
             "sample": f"first {Ts} of {w.T} tokens of {w.name}, whole path "
-                      f"(gate, layout, pack, combine), one thread, "
-                      f"{dt:.2f} s"}
+                      f"(gate, layout, pack, combine), one thread, {reps} "
+                      f"passes in {dt:.2f} s"}
 
 
 def _pct(a, q):
     return float(np.percentile(np.asarray(a), q))
+
+
+def _timed(fn, n, stream, before=None):
+    """Per-call durations (ms) of n calls of fn, HIP events on stream."""
+    import torch
+
+    evs = []
+    for _ in range(n):
+        if before is not None:
+            before()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def sequential_bounds(w, dev, stream, n=20) -> dict:
+    """The pack and the combine on the same buffers and bytes as the step,
+    with the slot table k*T + t instead of the expert-major permutation: every
+    destination (pack) or source (combine) row stream runs sequentially.
+    Same kernels, same byte counts and read:write mix; only the row order
+    differs, so this is the rate the order-free access pattern allows."""
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    if w.T * w.K * w.H * w.elem_bytes < (1 << 20):
+        return None
+    rows = torch.float32 if w.x_dtype == mi.F32 else torch.bfloat16
+    odt = torch.float32 if w.out_dtype == mi.F32 else torch.bfloat16
+    cfg = moe.make_cfg(w.T, w.H, w.E, w.K, w.R, w.N, w.x_dtype, w.out_dtype,
+                       w.renorm)
+    T, K = w.T, w.K
+    slots = (torch.arange(K, dtype=torch.int32, device=dev)[None, :] * T +
+             torch.arange(T, dtype=torch.int32, device=dev)[:, None])
+    slots = slots.contiguous().view(-1)
+    x = torch.randn((T, w.H), device=dev).to(rows)
+    send = torch.empty((T * K, w.H), dtype=rows, device=dev)
+    out = torch.empty((T, w.H), dtype=odt, device=dev)
+    wt = torch.full((T * K,), 1.0 / K, dtype=torch.float32, device=dev)
+    idx = torch.zeros(T * K, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        moe.moe_dispatch_pack(cfg, x, slots, send, stream)
+        moe.moe_combine(cfg, send, slots, wt, idx, None, out, stream)
+    pk, cb = [], []
+    for _ in range(n):  # pack then combine, as in a step
+        pk += _timed(lambda: moe.moe_dispatch_pack(cfg, x, slots, send,
+                                                   stream), 1, stream)
+        cb += _timed(lambda: moe.moe_combine(cfg, send, slots, wt, idx, None,
+                                             out, stream), 1, stream)
+    kb = kernel_bytes(w)
+    kb["combine"] -= 4 * w.E  # no expert scales read here
+    return {"slots": "k*T + t",
+            "pack_gbps": kb["pack"] / (_pct(pk, 50) * 1e-3) / 1e9,
+            "combine_gbps": kb["combine"] / (_pct(cb, 50) * 1e-3) / 1e9,
+            "pack_ms": _pct(pk, 50), "combine_ms": _pct(cb, 50)}
+
+
+# The fused call takes the one-launch decode kernel after the gate for
+# batches of at most 1024 tokens and 4096 (token, slot) pairs (the
+# library's rule, stated in its decode kernel source).
+DECODE_MAX_T, DECODE_MAX_TK = 1024, 4096
+
+
+def config_line(w, dev, n=20) -> dict:
+    """One workload through moe_dispatch_combine: warm and cold-clean step
+    times, tokens/s, whole-path GB/s, and the dominant kernel's rate."""
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    d = mi.make_inputs(w)
+    rows = torch.float32 if w.x_dtype == mi.F32 else torch.bfloat16
+    odt = torch.float32 if w.out_dtype == mi.F32 else torch.bfloat16
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    cfg = moe.make_cfg(w.T, w.H, w.E, w.K, w.R, w.N, w.x_dtype, w.out_dtype,
+                       w.renorm)
+    x, lg = to_dev(d["x"]), to_dev(d["logits"])
+    del d["x"]
+    scale = None if d["expert_scale"] is None else to_dev(d["expert_scale"])
+    idx = torch.empty(w.T * w.K, dtype=torch.int32, device=dev)
+    wt = torch.empty(w.T * w.K, dtype=torch.float32, device=dev)
+    lay = moe.alloc_layout(cfg, dev)
+    send = torch.empty((w.T * w.K, w.H), dtype=rows, device=dev)
+    out = torch.empty((w.T, w.H), dtype=odt, device=dev)
+    ws = moe.alloc_workspace(cfg, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_dispatch_combine(cfg, x, lg, scale, idx, wt, lay, send, out,
+                                 ws)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    warm = _timed(step, n, stream)
+    clean = _timed(step, n, stream,
+                   before=lambda: flush.sum(dtype=torch.int64))
+    del flush
+    alg = w.algorithmic_bytes()
+    ms = _pct(warm, 50)
+    line = {"T": w.T, "H": w.H, "E": w.E, "K": w.K, "R": w.R, "N": w.N,
+            "ms_warm": ms, "ms_cold_clean": _pct(clean, 50),
+            "tokens_per_s": w.T / (ms * 1e-3),
+            "gbps": alg / (ms * 1e-3) / 1e9,
+            "frac_of_peak": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "frac_of_peak_cold_clean":
+                alg / (_pct(clean, 50) * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    gate = _pct(_timed(lambda: moe.moe_topk_gate(cfg, lg, idx, wt, stream),
+                       n, stream), 50)
+    if w.T <= DECODE_MAX_T and w.T * w.K <= DECODE_MAX_TK:
+        # gate, then one decode kernel: its time is the step minus the gate
+        dk = ms - gate
+        by = alg - w.T * (4 * w.E + 8 * w.K)  # less the gate's own bytes
+        line["dominant"] = {"kernel": "decode (layout+pack+combine)",
+                            "ms": dk, "gbps": by / (dk * 1e-3) / 1e9,
+                            "frac": by / (dk * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        line["gate_ms"] = gate
+    else:
+        lay_ms = _pct(_timed(lambda: moe.moe_dispatch_layout(
+            cfg, idx, lay, ws, stream), n, stream), 50)
+        pk, cb = [], []
+        for _ in range(n):  # in step order, so the cache state is a step's
+            pk += _timed(lambda: moe.moe_dispatch_pack(cfg, x, lay.slot_pos,
+                                                       send, stream), 1, stream)
+            cb += _timed(lambda: moe.moe_combine(cfg, send, lay.slot_pos, wt,
+                                                 idx, scale, out, stream),
+                         1, stream)
+        kb = kernel_bytes(w)
+        t = {"pack": _pct(pk, 50), "combine": _pct(cb, 50)}
+        dom = max(t, key=t.get)
+        line["steps_ms"] = {"gate": gate, "layout": lay_ms, **t}
+        line["dominant"] = {"kernel": dom, "ms": t[dom],
+                            "gbps": kb[dom] / (t[dom] * 1e-3) / 1e9,
+                            "frac": kb[dom] / (t[dom] * 1e-3) / 1e9 /
+                            HBM_PEAK_GBPS}
+    del x, lg, send, out, lay, ws, idx, wt
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return line
 
 
 def extras(w, step, stream, alg, dev) -> dict:
@@ -257,7 +425,9 @@ def extras(w, step, stream, alg, dev) -> dict:
     torch.cuda.synchronize()
     clean = [a.elapsed_time(b) for a, b in clean]
     del flush
-    # copy ceiling: 2 GiB device-to-device copies
+    seq = sequential_bounds(w, dev, stream)
+    # a plain 2 GiB device-to-device copy (torch), for context only: it
+    # moves bytes 1:1, a mix the pack and combine do not have
     src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -307,8 +477,8 @@ def extras(w, step, stream, alg, dev) -> dict:
                     "p90": _pct(cold, 90)},
         "cold_clean_ms": {"p10": _pct(clean, 10), "p50": _pct(clean, 50),
                           "p90": _pct(clean, 90)},
-        "copy_ceiling_gbps": copy_gbps,
-        "frac_of_copy_ceiling": alg / (med_w * 1e-3) / 1e9 / copy_gbps,
+        "sequential_bound": seq,
+        "device_copy_gbps": copy_gbps,
         "rocm": ver, "driver": driver, "torch": torch.__version__,
         "clocks": clocks,
     }
@@ -494,6 +664,7 @@ def main() -> int:
             "kernel": dom, "bound": "hbm", "achieved": achieved,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "traffic_source": traffic_source(dom, w.name, traffic),
             "alg_bytes_per_launch": kb[dom],
             "launch_ms": steps_ms[dom],
         }
@@ -506,6 +677,15 @@ def main() -> int:
 
     if not args.fused_only and not args.no_extras:
         result["extras"] = extras(w, step, stream, alg, dev)
+        # every workload through the same fused call, measured in this run
+        del send, out, lay, ws
+        torch.cuda.empty_cache()
+        configs = {}
+        for name in ("tiny", "mixtral", "qwen3_skewed", "deepseek_v3",
+                     "deepseek_v3_decode", "kimi"):
+            print(f"bench: config {name}", file=sys.stderr, flush=True)
+            configs[name] = config_line(mi.WORKLOADS[name], dev)
+        result["extras"]["configs"] = configs
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)

@@ -78,3 +78,22 @@ def test_counter_summaries_follow_the_sources(tmp_path, monkeypatch):
     assert bench.load_traffic("pack", "kimi") is None
     src.write_text("kernel v2")
     assert bench.load_traffic("pack", "deepseek_v3") is None
+
+
+def test_decode_rule_matches_the_library():
+    # bench.py reports the decode kernel for the batches the library sends
+    # to it; the two limits are read from the kernel source
+    import re
+    src = open(os.path.join(ROOT, "combine_moe_topk_amd", "csrc",
+                            "decode.hip")).read()
+    t = int(re.search(r"kDecodeMaxTokens = (\d+);", src).group(1))
+    tk = int(re.search(r"kDecodeMaxIds = (\d+);", src).group(1))
+    assert (bench.DECODE_MAX_T, bench.DECODE_MAX_TK) == (t, tk)
+
+
+def test_traffic_source_is_labelled(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "k.hip").write_text("kernel v1")
+    monkeypatch.setitem(bench.KERNEL_SOURCES, "pack", ["k.hip"])
+    assert "profiles/traffic.json" in bench.traffic_source("pack", "kimi", 1.0)
+    assert bench.traffic_source("pack", "kimi", None).startswith("none")
