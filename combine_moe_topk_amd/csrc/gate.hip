@@ -97,6 +97,33 @@ __device__ __forceinline__ double group_sum_f64(double v) {
   return v;
 }
 
+// The K-th largest of the 16 values of a DPP row (each lane's own value;
+// equal values ordered by lane), in every lane of the row: each lane counts
+// the lanes whose value ranks before its own, reading them one rotation at
+// a time (row_ror), and the lane of rank K-1 gives its value.
+template <int R>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x120 + R,
+                                               0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t row_kth_largest(uint32_t v, int K) {
+  const int me = threadIdx.x & 15;
+  int rank = 0;
+#define MOE_RANK_STEP(R)                                              \
+  {                                                                   \
+    const uint32_t o = row_ror<R>(v);                                 \
+    const int from = (int)row_ror<R>((uint32_t)me); /* o's lane */    \
+    rank += (o > v || (o == v && from < me)) ? 1 : 0;                 \
+  }
+  MOE_RANK_STEP(1) MOE_RANK_STEP(2) MOE_RANK_STEP(3) MOE_RANK_STEP(4)
+  MOE_RANK_STEP(5) MOE_RANK_STEP(6) MOE_RANK_STEP(7) MOE_RANK_STEP(8)
+  MOE_RANK_STEP(9) MOE_RANK_STEP(10) MOE_RANK_STEP(11) MOE_RANK_STEP(12)
+  MOE_RANK_STEP(13) MOE_RANK_STEP(14) MOE_RANK_STEP(15)
+#undef MOE_RANK_STEP
+  return group_min<16>(rank == K - 1 ? v : 0xFFFFFFFFu);
+}
+
 constexpr int kCache = 4;  // D: cached (key, position) pairs per lane
 
 // Sorted cache of a lane's best keys (key descending, position ascending).
@@ -109,26 +136,30 @@ struct Cache {
   int lp;         //   and its position
 
   // Insert (k, j); j comes in ascending order, so an equal key stays behind.
+  // Branch-free: c[i] = k beats entry i (monotone in i, the cache being
+  // sorted); entry i becomes entry i-1 where c[i-1], k where c[i] alone,
+  // and stays otherwise.
   __device__ __forceinline__ void insert(uint32_t k, int j) {
-    if (k <= key[kCache - 1]) return;
-    key[kCache - 1] = k;
-    pos[kCache - 1] = j;
+    bool c[kCache];
+#pragma unroll
+    for (int i = 0; i < kCache; ++i) c[i] = k > key[i];
 #pragma unroll
     for (int i = kCache - 1; i > 0; --i) {
-      if (key[i] > key[i - 1]) {
-        const uint32_t tk = key[i];
-        key[i] = key[i - 1];
-        key[i - 1] = tk;
-        const int tp = pos[i];
-        pos[i] = pos[i - 1];
-        pos[i - 1] = tp;
-      }
+      key[i] = c[i - 1] ? key[i - 1] : (c[i] ? k : key[i]);
+      pos[i] = c[i - 1] ? pos[i - 1] : (c[i] ? j : pos[i]);
     }
+    key[0] = c[0] ? k : key[0];
+    pos[0] = c[0] ? j : pos[0];
   }
 
-  // The D best pairs among those after (lk, lp); with first, all of them.
+  // The D best candidate pairs among those after (lk, lp); with first, all
+  // of them.  cand: bit j set when key j is a candidate.  A key position
+  // where no lane of the wave has a candidate is skipped as a whole (a
+  // wave-uniform branch), so the sorted inserts run only for positions
+  // that hold one somewhere in the wave.
   template <int C>
-  __device__ __forceinline__ void fill(const uint32_t *keys, bool first) {
+  __device__ __forceinline__ void fill(const uint32_t *keys, uint64_t cand,
+                                       bool first) {
 #pragma unroll
     for (int i = 0; i < kCache; ++i) {
       key[i] = 0u;
@@ -137,9 +168,11 @@ struct Cache {
     int found = 0;
 #pragma unroll
     for (int j = 0; j < C; ++j) {
+      const bool mine = (cand >> j) & 1;
+      if (!__any(mine)) continue;
       const uint32_t k = keys[j];
       const bool after = first || k < lk || (k == lk && j > lp);
-      if (k != 0u && after) {
+      if (mine && after) {
         insert(k, j);
         ++found;
       }
@@ -178,18 +211,42 @@ __global__ __launch_bounds__(256) void gate_kernel(
   if (!live) t = T - 1;
   const float *row = logits + (size_t)t * E;
 
-  // clamped loads (no branch): all C are in flight before the first use
+  // Clamped loads, all C issued before the first use.  The empty asm takes
+  // every loaded value as an operand, so each load's result is used
+  // unconditionally and the compiler cannot move a load into the branch of
+  // the padding select below (where it would wait for each load in turn:
+  // C memory round trips instead of one).
+  float v[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) v[j] = row[min(sub + j * G, E - 1)];
+#pragma unroll
+  for (int j = 0; j < C; ++j) asm volatile("" : "+v"(v[j]));
   uint32_t key[C];
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int e = sub + j * G;
-    const float v = row[min(e, E - 1)];
-    key[j] = e < E ? order_bits(v) : 0u;
+  for (int j = 0; j < C; ++j)
+    key[j] = sub + j * G < E ? order_bits(v[j]) : 0u;
+  // Candidates: keys at or above a threshold theta that at least K keys of
+  // the token reach, so the K best are all candidates.  theta is the K-th
+  // largest of the G lane maxima (16-lane groups) or their minimum (K = G,
+  // or wider groups): at least K lanes hold a key >= theta.  Padding keys
+  // (0) are never candidates.
+  uint32_t lane_max = 0u;
+#pragma unroll
+  for (int j = 0; j < C; ++j) lane_max = key[j] > lane_max ? key[j] : lane_max;
+  uint32_t theta;
+  if constexpr (G == 16) {
+    theta = K < 16 ? row_kth_largest(lane_max, K) : group_min<16>(lane_max);
+  } else {
+    theta = group_min<G>(lane_max);
   }
+  uint64_t cmask = 0;  // bit j: key j is a candidate
+#pragma unroll
+  for (int j = 0; j < C; ++j)
+    cmask |= (key[j] != 0u && key[j] >= theta) ? (1ull << j) : 0ull;
   Cache cache;
   cache.lk = 0u;
   cache.lp = 0;
-  cache.fill<C>(key, true);
+  cache.fill<C>(key, cmask, true);
 
   int my_e = 0;
   float my_l = 0.0f;
@@ -207,7 +264,7 @@ __global__ __launch_bounds__(256) void gate_kernel(
     if (cand == win) cache.pop();  // the one lane holding the winner
     const bool refill = cache.n == 0 && cache.more;
     if (__any(refill)) {
-      if (refill) cache.fill<C>(key, false);
+      if (refill) cache.fill<C>(key, cmask, false);
     }
   }
 
