@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
     "combine": ["combine_moe_topk_amd/csrc/combine.hip",
                 "combine_moe_topk_amd/csrc/row_io.h"],
     "assign": ["combine_moe_topk_amd/csrc/assign.hip"],
+    "gate": ["combine_moe_topk_amd/csrc/gate.hip"],
     "pack_nodes": ["combine_moe_topk_amd/csrc/pack.hip"],
     "forward": ["combine_moe_topk_amd/csrc/nodes.hip"],
     "partial": ["combine_moe_topk_amd/csrc/nodes.hip",

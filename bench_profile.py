@@ -4,15 +4,17 @@
   python bench_profile.py traffic <fetch.db> <write.db> --workload NAME \
         --calib-mib MIB --cmd-fetch "<command>" --cmd-write "<command>"
   python bench_profile.py lds <results.db> <out.md> --cmd "<command>"
-  python bench_profile.py valu <results.db> --workload NAME --cmd "<command>"
+  python bench_profile.py valu <results.db> --workload NAME --cmd "<command>" \
+        [--role assign|gate]
 
 `trace` writes per-kernel duration statistics from a --kernel-trace run.
 `lds` summarises a run with SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE and
 SQ_INSTS_LDS: per kernel, the cycles LDS spent on bank conflicts against the
 cycles it was busy with indexed accesses.
-`valu` reads a run of `bench.py --path assign` with SQ_INSTS_VALU and
-SQ_INSTS_SALU and records the vector instructions one moe_assign_tasks call
-issues (its two kernels) in profiles/valu.json, with the source hash.
+`valu` reads a run with SQ_INSTS_VALU and SQ_INSTS_SALU (`bench.py --path
+assign`, or any run for the gate) and records the instructions one
+moe_assign_tasks call (its two kernels) or one gate launch issues, in total
+and per wave, in profiles/valu.json with the source hash.
 `traffic` reads a FETCH_SIZE run and a WRITE_SIZE run of
 `bench.py --fused-only ... --copy-calib-mib MIB`, scales each counter by what
 it reads for the calibration copy (a device copy of MIB MiB, which reads and
@@ -189,32 +191,47 @@ def lds(db: str, out: str, cmd: str) -> None:
         f.write("\n".join(lines))
 
 
-def valu(db: str, workload: str, cmd: str) -> None:
+VALU_KERNELS = {"assign": ("assign_kernel", "expert_tables_kernel"),
+                "gate": ("gate_kernel",)}
+
+
+def valu(db: str, workload: str, cmd: str, role: str = "assign") -> None:
     c = sqlite3.connect(db)
     per = collections.defaultdict(lambda: collections.defaultdict(list))
-    for n, counter, v in c.execute(
-            "select kernel_name, counter_name, value from counters_collection"):
+    waves = collections.defaultdict(list)
+    for n, counter, v, grid in c.execute(
+            "select kernel_name, counter_name, value, grid_size from "
+            "counters_collection"):
         per[short(n)][counter].append(v)
+        if counter == "SQ_INSTS_VALU":
+            waves[short(n)].append(grid / 64.0)
     parts = {k: {ctr: sum(v) / len(v) for ctr, v in d.items()}
-             for k, d in per.items()
-             if k.startswith(("assign_kernel", "expert_tables_kernel"))}
+             for k, d in per.items() if k.startswith(VALU_KERNELS[role])}
+    for k, d in parts.items():
+        d["waves"] = sum(waves[k]) / len(waves[k])
     total = sum(d.get("SQ_INSTS_VALU", 0.0) for d in parts.values())
     path = os.path.join(PROFILES, "valu.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
-    data[f"assign/{workload}"] = {
+    data[f"{role}/{workload}"] = {
         "valu_insts_per_call": total, "kernels": parts,
-        "source_sha": bench.source_digest(bench.KERNEL_SOURCES["assign"])}
+        "source_sha": bench.source_digest(bench.KERNEL_SOURCES[role])}
     with open(path, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
-    md = [f"# Vector instructions of moe_assign_tasks: {workload}\n",
+    title = {"assign": "moe_assign_tasks", "gate": "moe_topk_gate"}[role]
+    md = [f"# Vector instructions of {title}: {workload}\n",
           "Command:\n", f"    {cmd}\n",
-          "Wave-level instruction counts per dispatch (averaged):\n", "```",
-          f"{'kernel':40s} {'SQ_INSTS_VALU':>14s} {'SQ_INSTS_SALU':>14s}"]
+          "Instruction counts per dispatch (averaged), and per wave "
+          "(launched waves: grid size / 64):\n", "```",
+          f"{'kernel':40s} {'SQ_INSTS_VALU':>14s} {'SQ_INSTS_SALU':>14s} "
+          f"{'waves':>8s} {'VALU/wave':>10s} {'SALU/wave':>10s}"]
     for k, d in sorted(parts.items()):
+        w = d.get("waves", 0.0) or 1.0
         md.append(f"{k:40s} {d.get('SQ_INSTS_VALU', 0):14.0f} "
-                  f"{d.get('SQ_INSTS_SALU', 0):14.0f}")
+                  f"{d.get('SQ_INSTS_SALU', 0):14.0f} {w:8.0f} "
+                  f"{d.get('SQ_INSTS_VALU', 0) / w:10.1f} "
+                  f"{d.get('SQ_INSTS_SALU', 0) / w:10.1f}")
     md.append("```\n")
-    with open(os.path.join(PROFILES, f"valu_assign_{workload}.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"valu_{role}_{workload}.md"), "w") as f:
         f.write("\n".join(md))
 
 
@@ -233,6 +250,7 @@ def main() -> None:
     v.add_argument("db")
     v.add_argument("--workload", default="deepseek_v3")
     v.add_argument("--cmd", required=True)
+    v.add_argument("--role", default="assign", choices=("assign", "gate"))
     r = sub.add_parser("traffic")
     r.add_argument("fetch_db")
     r.add_argument("write_db")
@@ -256,7 +274,7 @@ def main() -> None:
     elif a.what == "lds":
         lds(a.db, a.out, a.cmd)
     elif a.what == "valu":
-        valu(a.db, a.workload, a.cmd)
+        valu(a.db, a.workload, a.cmd, a.role)
     else:
         traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
                 a.cmd_write, a.path, a.crossings, a.part_bytes, a.capacity,

@@ -9,20 +9,25 @@
 // expert index; -0.0 ranks equal to +0.0.
 //
 // Layout: a group of G lanes (16, 32 or 64) owns one token.  Lane `sub` of
-// the group holds the logits of experts sub, sub+G, sub+2G, ... as 32-bit
-// order-preserving keys (larger key = larger logit) and a sorted cache of its
-// D best (key, position) pairs, ordered by key descending, position
-// ascending.  A round takes the group maximum of the cache heads, then the
-// group minimum of the expert indices holding it, so "larger logit, then
-// lower index" wins; the winning lane pops its head.  A lane whose cache runs
-// empty refills it with the D best pairs strictly after the last one it gave
-// out (in the same order), so no key is ever cleared; refills run under a
-// wave-uniform branch and are rare (a lane empties only after D wins).
-// Group reductions are DPP inside 16-lane rows (quad_perm, half-mirror,
-// mirror: every lane of the row ends with the row's result) and readlane
-// across rows, with no LDS permutes.  G is the smallest width that keeps at
-// most 64 keys per lane and K <= G (the reductions are then shared by the
-// 64/G tokens of a wave).
+// the group holds the logits of experts sub, sub+G, sub+2G, ...  The path:
+//
+//  1. Threshold.  theta is a value that at least K of the token's logits
+//     reach, so the K best are all at or above it: in each 16-lane row, the
+//     ceil(K / rows)-th largest of the lanes' maxima (ranked with DPP
+//     rotations), then the minimum over the group's rows.
+//  2. Compaction.  The logits at or above theta (the candidates, typically
+//     K to 2K of them) are written to LDS as 64-bit keys, (order-preserving
+//     bits of the logit) << 32 | ~expert, so that a larger key means a larger
+//     logit, then a lower index.  Each lane's slice of the list comes from a
+//     DPP scan of the lanes' candidate counts.
+//  3. Rank.  Lane i takes entry i (and entry i + G when there are more than
+//     G candidates) and counts the entries with a larger key: that is its
+//     rank, and ranks below K are the output, written in rank order.
+//
+// A wave whose groups hold more than 2G candidates (many equal logits), or
+// a theta of -inf, takes the general path instead: each lane keeps a sorted
+// cache of its best candidates and K rounds of DPP group maxima pick the
+// winners one at a time.  Both give the same result; the tests cover each.
 #include "moe_internal.h"
 
 namespace moe {
@@ -51,6 +56,11 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF,
                                                false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 
 // Combine the four 16-lane rows' results for groups of G = 32 or 64 lanes.
 template <int G, bool MAX>
@@ -68,6 +78,27 @@ __device__ __forceinline__ uint32_t across_rows(uint32_t v) {
       return (threadIdx.x & 32) ? b : a;
     } else {
       return MAX ? (a > b ? a : b) : (a < b ? a : b);
+    }
+  }
+}
+
+// Same for floats, by comparison (no NaN reaches these).
+template <int G, bool MAX>
+__device__ __forceinline__ float across_rows_f(float v) {
+  if constexpr (G == 16) {
+    return v;
+  } else {
+    const int iv = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(iv, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(iv, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(iv, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(iv, 48));
+    const float a = MAX ? (r1 > r0 ? r1 : r0) : (r1 < r0 ? r1 : r0);
+    const float b = MAX ? (r3 > r2 ? r3 : r2) : (r3 < r2 ? r3 : r2);
+    if constexpr (G == 32) {
+      return (threadIdx.x & 32) ? b : a;
+    } else {
+      return MAX ? (b > a ? b : a) : (b < a ? b : a);
     }
   }
 }
@@ -90,6 +121,17 @@ __device__ __forceinline__ uint32_t group_min(uint32_t v) {
   return across_rows<G, false>(v);
 }
 
+// Row (16-lane) maximum or minimum of floats, in every lane of the row.
+template <bool MAX>
+__device__ __forceinline__ float row_reduce_f(float c) {
+  c = MAX ? fmaxf(c, dppf<kDppQuadXor1>(c)) : fminf(c, dppf<kDppQuadXor1>(c));
+  c = MAX ? fmaxf(c, dppf<kDppQuadXor2>(c)) : fminf(c, dppf<kDppQuadXor2>(c));
+  c = MAX ? fmaxf(c, dppf<kDppHalfMirror>(c))
+          : fminf(c, dppf<kDppHalfMirror>(c));
+  c = MAX ? fmaxf(c, dppf<kDppMirror>(c)) : fminf(c, dppf<kDppMirror>(c));
+  return c;
+}
+
 template <int G>
 __device__ __forceinline__ double group_sum_f64(double v) {
 #pragma unroll
@@ -97,36 +139,62 @@ __device__ __forceinline__ double group_sum_f64(double v) {
   return v;
 }
 
-// The K-th largest of the 16 values of a DPP row (each lane's own value;
-// equal values ordered by lane), in every lane of the row: each lane counts
-// the lanes whose value ranks before its own, reading them one rotation at
-// a time (row_ror), and the lane of rank K-1 gives its value.
 template <int R>
-__device__ __forceinline__ uint32_t row_ror(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x120 + R,
-                                               0xF, 0xF, false);
+__device__ __forceinline__ float row_ror_f(float v) {
+  return dppf<0x120 + R>(v);
 }
 
-__device__ __forceinline__ uint32_t row_kth_largest(uint32_t v, int K) {
-  const int me = threadIdx.x & 15;
-  int rank = 0;
-#define MOE_RANK_STEP(R)                                              \
-  {                                                                   \
-    const uint32_t o = row_ror<R>(v);                                 \
-    const int from = (int)row_ror<R>((uint32_t)me); /* o's lane */    \
-    rank += (o > v || (o == v && from < me)) ? 1 : 0;                 \
-  }
+// The kk-th largest of the 16 values of a DPP row (as a multiset), in every
+// lane of the row.  A lane whose value has fewer than kk strictly larger
+// values in the row holds a value >= the kk-th largest, and the kk-th
+// largest itself is such a value, so it is the smallest of them.  The
+// larger values are counted one row_ror rotation at a time.
+__device__ __forceinline__ float row_kth_largest(float v, int kk) {
+  int gt = 0;
+#define MOE_RANK_STEP(R) gt += row_ror_f<R>(v) > v ? 1 : 0;
   MOE_RANK_STEP(1) MOE_RANK_STEP(2) MOE_RANK_STEP(3) MOE_RANK_STEP(4)
   MOE_RANK_STEP(5) MOE_RANK_STEP(6) MOE_RANK_STEP(7) MOE_RANK_STEP(8)
   MOE_RANK_STEP(9) MOE_RANK_STEP(10) MOE_RANK_STEP(11) MOE_RANK_STEP(12)
   MOE_RANK_STEP(13) MOE_RANK_STEP(14) MOE_RANK_STEP(15)
 #undef MOE_RANK_STEP
-  return group_min<16>(rank == K - 1 ? v : 0xFFFFFFFFu);
+  return row_reduce_f<false>(gt < kk ? v : __builtin_huge_valf());
+}
+
+// Inclusive sum over the lanes of a group (DPP: row_shr inside 16-lane rows,
+// then row_bcast:15 and row_bcast:31 across rows).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+template <int G>
+__device__ __forceinline__ int group_inclusive_scan(int v) {
+  v = dpp_add<0x111, 0xF>(v);
+  v = dpp_add<0x112, 0xF>(v);
+  v = dpp_add<0x114, 0xF>(v);
+  v = dpp_add<0x118, 0xF>(v);
+  if constexpr (G >= 32) v = dpp_add<0x142, 0xA>(v);  // into rows 1 and 3
+  if constexpr (G == 64) v = dpp_add<0x143, 0xC>(v);  // into rows 2 and 3
+  return v;
+}
+
+// Orders the LDS accesses of one wave (its lanes exchange data through
+// LDS; no other wave touches that region).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Candidate key: larger means larger logit, then lower expert index; 0 is
+// below every real key (the smallest, -inf, has high word 0x007FFFFF).
+__device__ __forceinline__ uint64_t cand_key(float v, int e) {
+  return ((uint64_t)order_bits(v) << 32) | (uint32_t)~e;
 }
 
 constexpr int kCache = 4;  // D: cached (key, position) pairs per lane
 
-// Sorted cache of a lane's best keys (key descending, position ascending).
+// Sorted cache of a lane's best keys (key descending, position ascending),
+// for the general path.
 struct Cache {
   uint32_t key[kCache];
   int pos[kCache];
@@ -155,8 +223,7 @@ struct Cache {
   // The D best candidate pairs among those after (lk, lp); with first, all
   // of them.  cand: bit j set when key j is a candidate.  A key position
   // where no lane of the wave has a candidate is skipped as a whole (a
-  // wave-uniform branch), so the sorted inserts run only for positions
-  // that hold one somewhere in the wave.
+  // wave-uniform branch).
   template <int C>
   __device__ __forceinline__ void fill(const uint32_t *keys, uint64_t cand,
                                        bool first) {
@@ -194,13 +261,50 @@ struct Cache {
   }
 };
 
-// C keys per lane.  Keys of experts >= E are 0, below every real key (the
-// smallest finite logit has key 0x00800000), and never enter a cache.
-template <int G, int C>
+// The per-lane outcome: up to two selected experts, each with its output
+// position (rank), expert index and logit.
+struct Picks {
+  int r0, e0, r1, e1;
+  float l0, l1;
+  bool on0, on1;
+};
+
+// Rank the compacted candidates of the lane's group.  Lane sub takes entry
+// sub (TWO: and entry sub + G); n entries are compared, n a multiple of 4
+// and the same for the whole wave.  Empty entries hold 0, which every
+// candidate beats, so an empty entry's rank is at least M >= K.
+template <int G, bool TWO>
+__device__ __forceinline__ void rank_entries(const uint64_t *ent, int sub,
+                                             int n, int K, Picks &p) {
+  const uint64_t a = ent[sub];
+  const uint64_t b = TWO ? ent[sub + G] : 0ull;
+  int ra = 0, rb = 0;
+  for (int i = 0; i < n; i += 4) {
+    const ulonglong2 x = *reinterpret_cast<const ulonglong2 *>(ent + i);
+    const ulonglong2 y = *reinterpret_cast<const ulonglong2 *>(ent + i + 2);
+    ra += (x.x > a) + (x.y > a) + (y.x > a) + (y.y > a);
+    if constexpr (TWO) rb += (x.x > b) + (x.y > b) + (y.x > b) + (y.y > b);
+  }
+  p.on0 = ra < K;
+  p.r0 = ra;
+  p.e0 = (int)~(uint32_t)a;
+  p.l0 = from_order_bits((uint32_t)(a >> 32));
+  p.on1 = TWO && rb < K;
+  p.r1 = rb;
+  p.e1 = (int)~(uint32_t)b;
+  p.l1 = from_order_bits((uint32_t)(b >> 32));
+}
+
+// C keys per lane; FULL: E == G * C (no padding keys, unclamped loads).
+template <int G, int C, bool FULL>
 __global__ __launch_bounds__(256) void gate_kernel(
     const float *__restrict__ logits, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, int T, int E, int K, int renorm) {
   constexpr int kTokensPerBlock = 256 / G;
+  constexpr int kCap = 2 * G;        // LDS entries per group
+  constexpr int kStride = kCap + 2;  // padded: groups start on other banks
+  __shared__ __align__(16) uint64_t s_ent[4][(64 / G) * kStride];
+
   const int sub = threadIdx.x & (G - 1);
   int t = blockIdx.x * kTokensPerBlock + threadIdx.x / G;
   // groups past the last token compute on token T-1 and store nothing, so
@@ -211,117 +315,190 @@ __global__ __launch_bounds__(256) void gate_kernel(
   if (!live) t = T - 1;
   const float *row = logits + (size_t)t * E;
 
-  // Clamped loads, all C issued before the first use.  The empty asm takes
-  // every loaded value as an operand, so each load's result is used
-  // unconditionally and the compiler cannot move a load into the branch of
-  // the padding select below (where it would wait for each load in turn:
-  // C memory round trips instead of one).
+  // All C loads are issued before the first use.  The empty asm takes every
+  // loaded value as an operand, so the compiler cannot move a load into the
+  // branch of a later select (where it would wait for each load in turn).
+  // Padding keys (expert >= E) become -inf.
   float v[C];
+  if constexpr (FULL) {
+    const float *base = row + sub;
 #pragma unroll
-  for (int j = 0; j < C; ++j) v[j] = row[min(sub + j * G, E - 1)];
+    for (int j = 0; j < C; ++j) v[j] = base[j * G];
+  } else {
+#pragma unroll
+    for (int j = 0; j < C; ++j) v[j] = row[min(sub + j * G, E - 1)];
+  }
 #pragma unroll
   for (int j = 0; j < C; ++j) asm volatile("" : "+v"(v[j]));
-  uint32_t key[C];
+  if constexpr (!FULL) {
 #pragma unroll
-  for (int j = 0; j < C; ++j)
-    key[j] = sub + j * G < E ? order_bits(v[j]) : 0u;
-  // Candidates: keys at or above a threshold theta that at least K keys of
-  // the token reach, so the K best are all candidates.  theta is the K-th
-  // largest of the G lane maxima (16-lane groups) or their minimum (K = G,
-  // or wider groups): at least K lanes hold a key >= theta.  Padding keys
-  // (0) are never candidates.
-  uint32_t lane_max = 0u;
-#pragma unroll
-  for (int j = 0; j < C; ++j) lane_max = key[j] > lane_max ? key[j] : lane_max;
-  uint32_t theta;
-  if constexpr (G == 16) {
-    theta = K < 16 ? row_kth_largest(lane_max, K) : group_min<16>(lane_max);
-  } else {
-    theta = group_min<G>(lane_max);
+    for (int j = 0; j < C; ++j)
+      v[j] = sub + j * G < E ? v[j] : -__builtin_huge_valf();
   }
-  uint64_t cmask = 0;  // bit j: key j is a candidate
-#pragma unroll
-  for (int j = 0; j < C; ++j)
-    cmask |= (key[j] != 0u && key[j] >= theta) ? (1ull << j) : 0ull;
-  Cache cache;
-  cache.lk = 0u;
-  cache.lp = 0;
-  cache.fill<C>(key, cmask, true);
 
-  int my_e = 0;
-  float my_l = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    const uint32_t head = cache.n > 0 ? cache.key[0] : 0u;
-    const uint32_t m = group_max<G>(head);
-    const uint32_t cand = (cache.n > 0 && head == m)
-                              ? (uint32_t)(sub + cache.pos[0] * G)
-                              : 0xFFFFFFFFu;
-    const uint32_t win = group_min<G>(cand);
-    if (sub == k) {
-      my_e = (int)win;
-      my_l = from_order_bits(m);
+  float lmax = v[0];
+#pragma unroll
+  for (int j = 1; j < C; ++j) lmax = fmaxf(lmax, v[j]);  // v_max3_f32
+  constexpr int kRows = G / 16;
+  const int kk = (K + kRows - 1) / kRows;  // <= 16, as K <= G
+  const float theta =
+      across_rows_f<G, false>(row_kth_largest(lmax, kk));
+  const float mx = across_rows_f<G, true>(row_reduce_f<true>(lmax));
+
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < C; ++j) cnt += v[j] >= theta ? 1 : 0;
+  const int incl = group_inclusive_scan<G>(cnt);
+  // the most candidates of any group in the wave (a group's count is the
+  // inclusive sum at its last lane)
+  int Mw = 0;
+#pragma unroll
+  for (int g = 0; g < 64 / G; ++g) {
+    const int mg = __builtin_amdgcn_readlane(incl, g * G + G - 1);
+    Mw = mg > Mw ? mg : Mw;
+  }
+  // padding keys are -inf: a theta of -inf would take them in
+  const bool fast =
+      Mw <= kCap && (FULL || !__any(theta == -__builtin_huge_valf()));
+
+  Picks p;
+  if (fast) {
+    uint64_t *ent =
+        &s_ent[threadIdx.x >> 6][((threadIdx.x & 63) / G) * kStride];
+    ent[sub] = 0ull;
+    ent[sub + G] = 0ull;
+    wave_lds_sync();
+    int pos = incl - cnt;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if (v[j] >= theta) {
+        ent[pos] = cand_key(v[j], sub + j * G);
+        ++pos;
+      }
     }
-    if (cand == win) cache.pop();  // the one lane holding the winner
-    const bool refill = cache.n == 0 && cache.more;
-    if (__any(refill)) {
-      if (refill) cache.fill<C>(key, cmask, false);
+    wave_lds_sync();
+    const int n = (Mw + 3) & ~3;
+    if (Mw <= G) {
+      rank_entries<G, false>(ent, sub, n, K, p);
+    } else {
+      rank_entries<G, true>(ent, sub, n, K, p);
+    }
+  } else {
+    uint32_t key[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      key[j] = sub + j * G < E ? order_bits(v[j]) : 0u;
+    const uint32_t th = order_bits(theta);
+    uint64_t cmask = 0;  // bit j: key j is a candidate
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      cmask |= (key[j] != 0u && key[j] >= th) ? (1ull << j) : 0ull;
+    Cache cache;
+    cache.lk = 0u;
+    cache.lp = 0;
+    cache.fill<C>(key, cmask, true);
+    p.on0 = false;
+    p.on1 = false;
+    p.r0 = sub;
+    p.e0 = 0;
+    p.l0 = 0.0f;
+    p.r1 = 0;
+    p.e1 = 0;
+    p.l1 = 0.0f;
+    for (int k = 0; k < K; ++k) {
+      const uint32_t head = cache.n > 0 ? cache.key[0] : 0u;
+      const uint32_t m = group_max<G>(head);
+      const uint32_t cand = (cache.n > 0 && head == m)
+                                ? (uint32_t)(sub + cache.pos[0] * G)
+                                : 0xFFFFFFFFu;
+      const uint32_t win = group_min<G>(cand);
+      if (sub == k) {
+        p.on0 = true;
+        p.e0 = (int)win;
+        p.l0 = from_order_bits(m);
+      }
+      if (cand == win) cache.pop();  // the one lane holding the winner
+      const bool refill = cache.n == 0 && cache.more;
+      if (__any(refill)) {
+        if (refill) cache.fill<C>(key, cmask, false);
+      }
     }
   }
 
   // Weights in fp64: exp(l_k - l_max) / sum, rounded once to fp32.
-  const double mx = (double)__shfl(my_l, 0, G);
-  const double ex = (sub < K) ? exp((double)my_l - mx) : 0.0;
+  const double dmx = (double)mx;
+  const double x0 = p.on0 ? exp((double)p.l0 - dmx) : 0.0;
+  const double x1 = p.on1 ? exp((double)p.l1 - dmx) : 0.0;
   double denom = 0.0;
   if (renorm) {
-    denom = ex;
+    denom = x0 + x1;
   } else {
-    // every logit of the lane is in its keys (C*G >= E); -0.0 came back
-    // as +0.0, which gives the same exp(l - max)
+    // every logit of the lane is in v (C*G >= E); padding is -inf (exp 0)
 #pragma unroll
-    for (int j = 0; j < C; ++j)
-      if (sub + j * G < E) denom += exp((double)from_order_bits(key[j]) - mx);
+    for (int j = 0; j < C; ++j) denom += exp((double)v[j] - dmx);
   }
   denom = group_sum_f64<G>(denom);
 
-  if (live && sub < K) {
-    topk_idx[(size_t)t * K + sub] = my_e;
-    topk_w[(size_t)t * K + sub] = (float)(ex / denom);
+  if (live) {
+    if (p.on0) {
+      topk_idx[(size_t)t * K + p.r0] = p.e0;
+      topk_w[(size_t)t * K + p.r0] = (float)(x0 / denom);
+    }
+    if (p.on1) {
+      topk_idx[(size_t)t * K + p.r1] = p.e1;
+      topk_w[(size_t)t * K + p.r1] = (float)(x1 / denom);
+    }
   }
 }
 
 constexpr int kGateWaveTokens = 1024;  // up to here: one wave per token
 
-int pow2_ceil(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
-
 template <int G, int C>
-hipError_t launch_gc(const float *logits, int32_t *idx, float *w, int T,
-                     int E, int K, int renorm, hipStream_t s) {
+hipError_t launch_gc(bool full, const float *logits, int32_t *idx, float *w,
+                     int T, int E, int K, int renorm, hipStream_t s) {
   constexpr int tpb = 256 / G;
   const int grid = (T + tpb - 1) / tpb;
-  hipLaunchKernelGGL((gate_kernel<G, C>), dim3(grid), dim3(256), 0, s,
-                     logits, idx, w, T, E, K, renorm);
+  if (full) {
+    hipLaunchKernelGGL((gate_kernel<G, C, true>), dim3(grid), dim3(256), 0, s,
+                       logits, idx, w, T, E, K, renorm);
+  } else {
+    hipLaunchKernelGGL((gate_kernel<G, C, false>), dim3(grid), dim3(256), 0,
+                       s, logits, idx, w, T, E, K, renorm);
+  }
   return hipGetLastError();
 }
 
+// Keys per lane: 1, 2, 4, 8, 16, 28 (Kimi K2's E = 896 over 32 lanes), 32;
+// with 64 lanes also 48 and 64.
 template <int G>
-hipError_t launch_g(int C, const float *logits, int32_t *idx, float *w,
-                    int T, int E, int K, int renorm, hipStream_t s) {
+hipError_t launch_g(int C, bool full, const float *logits, int32_t *idx,
+                    float *w, int T, int E, int K, int renorm,
+                    hipStream_t s) {
   switch (C) {
-    case 1: return launch_gc<G, 1>(logits, idx, w, T, E, K, renorm, s);
-    case 2: return launch_gc<G, 2>(logits, idx, w, T, E, K, renorm, s);
-    case 4: return launch_gc<G, 4>(logits, idx, w, T, E, K, renorm, s);
-    case 8: return launch_gc<G, 8>(logits, idx, w, T, E, K, renorm, s);
-    case 16: return launch_gc<G, 16>(logits, idx, w, T, E, K, renorm, s);
-    case 32: return launch_gc<G, 32>(logits, idx, w, T, E, K, renorm, s);
-    case 48: return launch_gc<G, 48>(logits, idx, w, T, E, K, renorm, s);
-    case 56: return launch_gc<G, 56>(logits, idx, w, T, E, K, renorm, s);
-    case 64: return launch_gc<G, 64>(logits, idx, w, T, E, K, renorm, s);
-    default: return hipErrorInvalidValue;
+    case 1: return launch_gc<G, 1>(full, logits, idx, w, T, E, K, renorm, s);
+    case 2: return launch_gc<G, 2>(full, logits, idx, w, T, E, K, renorm, s);
+    case 4: return launch_gc<G, 4>(full, logits, idx, w, T, E, K, renorm, s);
+    case 8: return launch_gc<G, 8>(full, logits, idx, w, T, E, K, renorm, s);
+    case 16: return launch_gc<G, 16>(full, logits, idx, w, T, E, K, renorm, s);
+    case 28: return launch_gc<G, 28>(full, logits, idx, w, T, E, K, renorm, s);
+    case 32: return launch_gc<G, 32>(full, logits, idx, w, T, E, K, renorm, s);
+    default: break;
   }
+  if constexpr (G == 64) {
+    switch (C) {
+      case 48: return launch_gc<G, 48>(full, logits, idx, w, T, E, K, renorm, s);
+      case 64: return launch_gc<G, 64>(full, logits, idx, w, T, E, K, renorm, s);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+int keys_per_lane(int need) {
+  static const int kC[] = {1, 2, 4, 8, 16, 28, 32, 48, 64};
+  for (int c : kC)
+    if (c >= need) return c;
+  return 0;
 }
 
 }  // namespace
@@ -329,26 +506,22 @@ hipError_t launch_g(int C, const float *logits, int32_t *idx, float *w,
 hipError_t launch_gate(const moe_cfg &c, const float *logits,
                        int32_t *topk_idx, float *topk_w, hipStream_t stream) {
   if (c.T == 0) return hipSuccess;
-  // smallest group with at most 64 keys per lane and K <= G: with 4 or
-  // more waves per SIMD the kernel is bound by instruction issue, and narrow
-  // groups share the selection's reductions among more tokens.  With few
-  // tokens (at most one wave per SIMD at G = 64) it is bound by one wave's
-  // latency instead, and a whole wave per token, with 4x fewer keys per
-  // lane, is faster: 7.5 against 10.8 us for 128 tokens of the DeepSeek-V3
-  // shape, measured on MI355X.
+  // The narrowest group with at most 32 keys per lane and K <= G/2: narrow
+  // groups share the per-wave work among 64/G tokens, and with G >= 2K the
+  // threshold (the ceil(K/rows)-th largest lane maximum of each row) leaves
+  // few candidates.  With few tokens (at most one wave per SIMD at G = 64)
+  // the kernel is bound by one wave's latency instead, and a whole wave per
+  // token, with fewer keys per lane, is faster.
   int G = 16;
-  while (G < 64 && ((c.E + G - 1) / G > 64 || G < c.K)) G <<= 1;
+  while (G < 64 && ((c.E + G - 1) / G > 32 || 2 * c.K > G)) G <<= 1;
   if (c.T <= kGateWaveTokens) G = 64;
-  const int need = (c.E + G - 1) / G;  // keys per lane, <= 64
-  // keys per lane: a power of two up to 32, then 48, 56 or 64 (56 is the
-  // Kimi K2 shape, E = 896 over 16 lanes: no dead key slots)
-  int C = need <= 32 ? pow2_ceil(need) : (need <= 48 ? 48 : (need <= 56 ? 56 : 64));
-  if (C < 1) C = 1;
+  const int C = keys_per_lane((c.E + G - 1) / G);  // E <= 4096: C <= 64
+  const bool full = c.E == G * C;
   const int renorm = (c.flags & MOE_F_NO_RENORM) ? 0 : 1;
   switch (G) {
-    case 16: return launch_g<16>(C, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
-    case 32: return launch_g<32>(C, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
-    case 64: return launch_g<64>(C, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
+    case 16: return launch_g<16>(C, full, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
+    case 32: return launch_g<32>(C, full, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
+    case 64: return launch_g<64>(C, full, logits, topk_idx, topk_w, c.T, c.E, c.K, renorm, stream);
     default: return hipErrorInvalidValue;
   }
 }
