@@ -89,7 +89,7 @@ hipError_t launch_fused(const moe_cfg &c, const void *x, const float *logits,
   hipError_t e = launch_gate(c, logits, topk_idx, topk_w, stream);
   if (e != hipSuccess) return e;
   // a decode-sized batch: layout, pack and combine in one launch
-  if (decode_ok(c) && aligned16(topk_idx))
+  if (decode_ok(c))
     return launch_decode(c, x, topk_idx, topk_w, expert_scale, lay, send, out,
                          stream);
   e = launch_layout(c, topk_idx, lay, ws, stream);

@@ -18,9 +18,9 @@
 // and none takes under a few microseconds).  Two facts remove the grid-wide
 // dependencies between the steps:
 //   - a token's slots need only the expert ids of all tokens (T*K of them,
-//     a few KB): every workgroup loads them into LDS and derives the counts
-//     and offsets it needs with LDS histograms and a scan, instead of
-//     waiting for a layout launch;
+//     a few KB): every workgroup loads them and derives the counts and
+//     offsets it needs with LDS histograms and a scan, instead of waiting
+//     for a layout launch;
 //   - the combine of token t reads exactly the K send rows that the pack of
 //     token t wrote, so the workgroup that packs a token's rows combines
 //     them: after a workgroup barrier its threads read the rows back from
@@ -37,7 +37,7 @@ namespace moe {
 namespace {
 
 constexpr int kDecodeMaxTokens = 1024;
-constexpr int kDecodeMaxIds = 4096;       // T*K held in LDS
+constexpr int kDecodeMaxIds = 4096;       // T*K, held in registers
 constexpr size_t kDecodeMaxLds = 65536;   // bytes of LDS a workgroup may use
 constexpr int kDecodeBlock = 1024;
 constexpr int kDecodeWaves = kDecodeBlock / kWave;
@@ -87,42 +87,38 @@ struct DecodeOut {
   uint64_t *node_mask;
 };
 
-// Sum over the 64 lanes of a wave, in every lane: DPP exchanges inside each
-// 16-lane row (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
-// row_mirror: each step adds the partner group's sum), then the four rows.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+// Inclusive sum over the lanes of a wave (DPP: row_shr:1,2,4,8 inside
+// 16-lane rows, then row_bcast:15 into rows 1 and 3, row_bcast:31 into rows
+// 2 and 3).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
 }
-__device__ __forceinline__ int wave_sum(int v) {
-  v += dpp_i32<0xB1>(v);
-  v += dpp_i32<0x4E>(v);
-  v += dpp_i32<0x141>(v);
-  v += dpp_i32<0x140>(v);
-  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v = dpp_add<0x111, 0xF>(v);
+  v = dpp_add<0x112, 0xF>(v);
+  v = dpp_add<0x114, 0xF>(v);
+  v = dpp_add<0x118, 0xF>(v);
+  v = dpp_add<0x142, 0xA>(v);
+  v = dpp_add<0x143, 0xC>(v);
+  return v;
 }
 
-// 16-byte vectors of expert ids a thread loads up front (T*K <= 4096 ids
-// over at least 256 threads).
-constexpr int kIdVecs = kDecodeMaxIds / 4 / 256;
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// The expert ids of the T*K slots a thread holds: slot i = tid + j*B
+// (T*K <= 4096 over at least 256 threads: at most 16 a thread).
+constexpr int kIdsPerThread = kDecodeMaxIds / 256;
 
-// The T*K expert ids as 16-byte vectors (topk_idx is 16-byte aligned on
-// this path): vector v = tid + q*B, indexes clamped to the last whole
-// vector (values past nvec never used); the TK % 4 ids of a partial last
-// vector one by one (thread tid < TK % 4).  All loads issued together.
-struct IdLoad {
-  i32x4 v[kIdVecs];
-  int tail;
-  __device__ __forceinline__ void issue(const int32_t *topk_idx, int TK) {
-    const int nvec = TK / 4;
+struct Ids {
+  int32_t e[kIdsPerThread];
+
+  // ids written before this launch
+  __device__ __forceinline__ void load(const int32_t *topk_idx, int TK) {
     const int B = blockDim.x, tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < kIdVecs; ++q)
-      v[q] = ((const i32x4 *)topk_idx)[min(tid + q * B, max(nvec - 1, 0))];
-    tail = tid < TK % 4 ? topk_idx[nvec * 4 + tid] : 0;
+    for (int j = 0; j < kIdsPerThread; ++j)
+      if (j * B < TK) e[j] = tid + j * B < TK ? topk_idx[tid + j * B] : 0;
   }
+
 };
 
 // The batch-wide layout outputs, by workgroup 0: expert counts and offsets
@@ -130,12 +126,12 @@ struct IdLoad {
 // the tokens (64 tokens a word, set with LDS atomics, the bitmaps of the
 // layout kernels): distinct tokens per rank, node counts and offsets, and
 // every token's node mask and node slots.
-__device__ void decode_globals(const IdLoad &il, int T, int E, int K, int R,
+__device__ void decode_globals(const Ids &ids, int T, int E, int K, int R,
                                int N, uint32_t m_rank, uint32_t m_node,
                                uint32_t m_k, const DecodeOut &o,
                                uint64_t *sm) {
   const int tid = threadIdx.x, B = blockDim.x, lane = tid % kWave;
-  const int TK = T * K, nvec = TK / 4;
+  const int TK = T * K;
   const int TW = (T + kWave - 1) / kWave;  // 64-token words of a bitmap
   uint64_t *nbm = sm;                      // [N][TW]
   uint64_t *rbm = nbm + (size_t)N * TW;    // [R][TW]
@@ -158,13 +154,8 @@ __device__ void decode_globals(const IdLoad &il, int T, int E, int K, int R,
     atomicOr((unsigned long long *)&rbm[div_small(e, m_rank) * TW + w], bit);
   };
 #pragma unroll
-  for (int q = 0; q < kIdVecs; ++q) {
-    const int v = tid + q * B;
-    if (v >= nvec) break;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) add(4 * v + h, il.v[q][h]);
-  }
-  if (tid < TK % 4) add(nvec * 4 + tid, il.tail);
+  for (int j = 0; j < kIdsPerThread; ++j)
+    if (tid + j * B < TK) add(tid + j * B, ids.e[j]);
   __syncthreads();
   scan_lds(hist, E, eoff, wsum);  // ends with a barrier
   const int per_rank = E / R;
@@ -224,7 +215,7 @@ __device__ void decode_globals(const IdLoad &il, int T, int E, int K, int R,
   }
 }
 
-template <bool YB, bool OB, int KT>
+template <bool YB, bool OB>
 __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(
     const char *__restrict__ x, const int32_t *__restrict__ topk_idx,
     const float *__restrict__ topk_w, const float *__restrict__ scale,
@@ -232,19 +223,19 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(
     uint32_t m_node, uint32_t m_k, DecodeOut o, char *__restrict__ send,
     char *__restrict__ out) {
   extern __shared__ uint64_t sm64[];
-  const int TK = T * K, nvec = TK / 4;
-  const int tid = threadIdx.x, B = blockDim.x, lane = tid % kWave;
+  const int TK = T * K;
+  const int tid = threadIdx.x, B = blockDim.x;
   if (blockIdx.x == 0) {
-    IdLoad il;
-    il.issue(topk_idx, TK);
-    decode_globals(il, T, E, K, R, N, m_rank, m_node, m_k, o, sm64);
+    Ids ids;
+    ids.load(topk_idx, TK);
+    decode_globals(ids, T, E, K, R, N, m_rank, m_node, m_k, o, sm64);
     return;
   }
-  int32_t *ids = (int32_t *)sm64;   // [TK]
-  int32_t *sums = ids + TK;         // [2 * KT]: experts below e_k; tokens
-                                    //   before t holding e_k
-  int32_t *slot = sums + 2 * KT;    // [KT] token t's send rows
-  float *coef = (float *)(slot + KT);  // [KT] w * s of token t's slots
+  int32_t *hist = (int32_t *)sm64;  // [E] slots per expert
+  int32_t *hb = hist + E;           // [E] the same over the slots before t's
+  int32_t *eoff = hb + E;           // [E] exclusive prefix of hist
+  int32_t *slot = eoff + E;         // [32] token t's send rows
+  float *coef = (float *)(slot + 32);  // [32] w * s of token t's slots
 
   const int b = blockIdx.x - 1;
   const int t = b / P;
@@ -257,8 +248,8 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(
   // while the slots are derived), then the token's expert scales.
   const int my_e = tid < K ? topk_idx[mine + tid] : 0;
   const float my_w = tid < K ? topk_w[mine + tid] : 0.0f;
-  IdLoad il;
-  il.issue(topk_idx, TK);
+  Ids ids;
+  ids.load(topk_idx, TK);
   const int chunk = (U + P - 1) / P;
   const int u0 = part * chunk;
   const int u1 = min(U, u0 + chunk);
@@ -273,56 +264,30 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(
   const bool my_ok = tid < K && (unsigned)my_e < (unsigned)E;
   const float sc = (my_ok && scale) ? scale[my_e] : 1.0f;
 
-#pragma unroll
-  for (int q = 0; q < kIdVecs; ++q)
-    if (tid + q * B < nvec) ((i32x4 *)ids)[tid + q * B] = il.v[q];
-  if (tid < TK % 4) ids[nvec * 4 + tid] = il.tail;
-  if (tid < 2 * KT) sums[tid] = 0;
+  // slot of (t, k) = slots of experts below e_k + slots of e_k before t's:
+  // LDS histograms of every slot's expert and of the slots before t's (ids
+  // outside [0, E), which the gate never produces, are left out), then one
+  // wave's scan of the first
+  for (int i = tid; i < 2 * E; i += B) hist[i] = 0;
   __syncthreads();
-
-  // slot of (t, k) = experts below e_k over all slots + tokens before t
-  // holding e_k: one pass over this thread's ids per group of 8 slots,
-  // counted per lane, summed over the wave (DPP) and added into LDS
-  for (int k0 = 0; k0 < K; k0 += 8) {
-    int tgt[8], lt[8], eq[8];
+  auto count = [&](int i, int e) {
+    if ((unsigned)e >= (unsigned)E) return;
+    atomicAdd(&hist[e], 1);
+    if (i < mine) atomicAdd(&hb[e], 1);
+  };
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      tgt[k] = ids[mine + min(k0 + k, K - 1)];
-      lt[k] = eq[k] = 0;
-    }
-#pragma unroll
-    for (int q = 0; q < kIdVecs; ++q) {
-      if (q * B >= nvec) break;  // uniform
-      const int v = tid + q * B;
-      if (v < nvec) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int e = il.v[q][h];
-          const int early = 4 * v + h < mine ? 1 : 0;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            lt[k] += e < tgt[k] ? 1 : 0;
-            eq[k] += e == tgt[k] ? early : 0;
-          }
-        }
-      }
-    }
-    if (tid < TK % 4) {
-      const int early = nvec * 4 + tid < mine ? 1 : 0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        lt[k] += il.tail < tgt[k] ? 1 : 0;
-        eq[k] += il.tail == tgt[k] ? early : 0;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (k0 + k >= K) break;  // uniform
-      const int a = wave_sum(lt[k]), c = wave_sum(eq[k]);
-      if (lane == 0) {
-        if (a) atomicAdd(&sums[k0 + k], a);
-        if (c) atomicAdd(&sums[KT + k0 + k], c);
-      }
+  for (int j = 0; j < kIdsPerThread; ++j)
+    if (tid + j * B < TK) count(tid + j * B, ids.e[j]);
+  __syncthreads();
+  if (tid < kWave) {
+    const int per = (E + kWave - 1) / kWave;
+    const int lo = min(E, tid * per), hi = min(E, lo + per);
+    int local = 0;
+    for (int e = lo; e < hi; ++e) local += hist[e];
+    int run = wave_inclusive_scan(local) - local;
+    for (int e = lo; e < hi; ++e) {
+      eoff[e] = run;
+      run += hist[e];
     }
   }
   __syncthreads();
@@ -330,7 +295,7 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(
     int s = -1;
     float c = 0.0f;
     if (my_ok) {
-      s = sums[tid] + sums[KT + tid];
+      s = eoff[my_e] + hb[my_e];
       c = scale ? my_w * sc : my_w;  // fp32 product, as the combine kernel
     }
     slot[tid] = s;
@@ -342,7 +307,12 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(
   }
   __syncthreads();
 
-  // Pack: the token's row units, stored to each of its K send rows.
+  // Pack: the token's row units, stored to each of its K send rows.  The
+  // stores are non-temporal: the lines still serve the combine's reads
+  // below from the cache, and fewer dirty lines are left to write back when
+  // the kernel ends (7.7 against 8.1 us a launch for 128 tokens of the
+  // DeepSeek-V3 shape; with the device-scope bit as well the reads below
+  // missed the cache, 9.2 us).
   const int vend = u1 * kVecs;
 #pragma unroll
   for (int q = 0; q < kPre; ++q) {
@@ -350,14 +320,18 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(
     if (v >= vend) break;
     for (int k = 0; k < K; ++k) {
       const int s = slot[k];
-      if (s >= 0) ((u32x4 *)(send + (size_t)s * rbytes))[v] = xv[q];
+      if (s >= 0)
+        __builtin_nontemporal_store(xv[q],
+                                    (u32x4 *)(send + (size_t)s * rbytes) + v);
     }
   }
   for (int v = u0 * kVecs + tid + kPre * B; v < vend; v += B) {
     const u32x4 val = xsrc[v];
     for (int k = 0; k < K; ++k) {
       const int s = slot[k];
-      if (s >= 0) ((u32x4 *)(send + (size_t)s * rbytes))[v] = val;
+      if (s >= 0)
+        __builtin_nontemporal_store(val,
+                                    (u32x4 *)(send + (size_t)s * rbytes) + v);
     }
   }
   // The pack's stores are visible to every thread of the workgroup after
@@ -394,8 +368,8 @@ size_t decode_lds_bytes(const moe_cfg &c) {
   const size_t g = 8 * (size_t)(c.N + c.R) * TW +
                    4 * ((size_t)c.E + c.E + 1 + TW * c.N + c.N + 1 +
                         kDecodeWaves);
-  // token workgroups: ids, sums, slot, coef (KT <= 32)
-  const size_t w = 4 * ((size_t)c.T * c.K + 4 * 32);
+  // token workgroups: hist, hb, eoff, then slot and coef (K <= 32)
+  const size_t w = 4 * (3 * (size_t)c.E + 2 * 32);
   return std::max(g, w);
 }
 
@@ -428,22 +402,15 @@ hipError_t launch_decode(const moe_cfg &c, const void *x,
   const size_t lds = decode_lds_bytes(c);
   const dim3 grid(1 + c.T * P);  // workgroup 0: the batch-wide outputs
   const bool yb = c.x_dtype == MOE_BF16, ob = c.out_dtype == MOE_BF16;
-#define MOE_DECODE(YB_, OB_, KT_)                                           \
-  hipLaunchKernelGGL((decode_kernel<YB_, OB_, KT_>), grid, dim3(B), lds,     \
-                     stream, (const char *)x, topk_idx, topk_w, expert_scale, \
-                     c.T, c.E, c.K, c.R, c.N, U, P, m_rank, m_node, m_k, o,  \
+#define MOE_DECODE(YB_, OB_)                                                \
+  hipLaunchKernelGGL((decode_kernel<YB_, OB_>), grid, dim3(B), lds, stream, \
+                     (const char *)x, topk_idx, topk_w, expert_scale, c.T,  \
+                     c.E, c.K, c.R, c.N, U, P, m_rank, m_node, m_k, o,      \
                      (char *)send, (char *)out)
-#define MOE_DECODE_K(YB_, OB_)                  \
-  if (c.K <= 2) MOE_DECODE(YB_, OB_, 2);         \
-  else if (c.K <= 4) MOE_DECODE(YB_, OB_, 4);    \
-  else if (c.K <= 8) MOE_DECODE(YB_, OB_, 8);    \
-  else if (c.K <= 16) MOE_DECODE(YB_, OB_, 16);  \
-  else MOE_DECODE(YB_, OB_, 32);
-  if (yb && ob) { MOE_DECODE_K(true, true) }
-  else if (yb) { MOE_DECODE_K(true, false) }
-  else if (ob) { MOE_DECODE_K(false, true) }
-  else { MOE_DECODE_K(false, false) }
-#undef MOE_DECODE_K
+  if (yb && ob) MOE_DECODE(true, true);
+  else if (yb) MOE_DECODE(true, false);
+  else if (ob) MOE_DECODE(false, true);
+  else MOE_DECODE(false, false);
 #undef MOE_DECODE
   return hipGetLastError();
 }

@@ -465,6 +465,41 @@ def test_fused_decode_path(case):
     assert torch.equal(send, send2) and torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("T,K", [(1, 3), (37, 8)])
+def test_fused_decode_ids_4byte_aligned(T, K):
+    # expert ids and weights in views that start 4 bytes into their storage
+    # (and T*K = 3, under one 16-byte vector): the decode kernel reads ids one
+    # by one, so alignment and short lengths are the caller's to choose
+    w = mi.Workload("decode", T=T, H=256, E=64, K=K, R=8, N=2)
+    d = mi.make_inputs(w)
+    ref = oracle.dispatch_combine(d["x"], d["logits"], K, 8, 2,
+                                  d["expert_scale"], w.out_dtype)
+    cfg = cfg_of(w)
+    idx_store = torch.full((T * K + 1,), -7, dtype=torch.int32, device="cuda")
+    wt_store = torch.zeros(T * K + 1, dtype=torch.float32, device="cuda")
+    idx, wt = idx_store[1:], wt_store[1:]
+    assert idx.data_ptr() % 16 == 4
+    lay = moe.alloc_layout(cfg)
+    send = torch.empty((T * K, w.H), dtype=row_dtype(w), device="cuda")
+    out = torch.empty((T, w.H), dtype=out_dtype(w), device="cuda")
+    ws = moe.alloc_workspace(cfg)
+    moe.moe_dispatch_combine(cfg, dev(d["x"]), dev(d["logits"]),
+                             dev(d["expert_scale"]), idx, wt, lay, send, out,
+                             ws)
+    assert moe.moe_read_device_error(ws) == 0
+    assert int(idx_store[0]) == -7
+    res = layout_to_host(lay, T, K, 2)
+    res.update(topk_idx=host(idx).reshape(T, K), topk_w=host(wt).reshape(T, K))
+    check_gate(res, ref["topk_idx"], ref["topk_w"])
+    check_layout(res, ref)
+    np.testing.assert_array_equal(host(send), ref["send"])
+    coef = ref["topk_w"].astype(np.float64) * \
+        d["expert_scale"][ref["topk_idx"]]
+    check_out(host(out), ref["out_exact"],
+              term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef),
+              w.out_dtype)
+
+
 def test_identity_experts_return_input():
     # renormalised weights and identity experts: out == x (bf16), the dispatch
     # permutation inverting exactly under the combine
