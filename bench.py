@@ -499,7 +499,8 @@ def main() -> int:
     ap.add_argument("--layout-tile", type=int, default=0,
                     help="tokens per layout workgroup (0: library default)")
     ap.add_argument("--path", default="flat",
-                    choices=("flat", "two_leg", "fp8", "capacity", "assign"))
+                    choices=("flat", "two_leg", "fp8", "capacity", "assign",
+                             "pack_orders"))
     ap.add_argument("--rho", type=float, default=0.5,
                     help="replica budget of --path assign")
     ap.add_argument("--gamma", type=float, default=1.25,
@@ -558,6 +559,8 @@ def main() -> int:
     if args.path == "assign":
         del send
         return assign_path(args, w, d, cfg, lg, idx, wt, stream)
+    if args.path == "pack_orders":
+        return pack_orders(args, w, cfg, x, lg, idx, wt, lay, send, ws, stream)
     if args.path == "capacity":
         del send
         return capacity_path(args, w, cfg, x, lg, scale, idx, wt, out, stream)
@@ -692,6 +695,39 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)
 
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def pack_orders(args, w, cfg, x, lg, idx, wt, lay, send, ws, stream) -> int:
+    """The pack kernel on the step's buffers with two destination orders:
+    args.warmup launches of each, then args.steps launches with the
+    layout's expert-major slots, then args.steps with slot k*T + t (every
+    destination stream sequential).  Under rocprofv3 the dispatches come in
+    that order (bench_profile.py pack_orders splits them).  One JSON line."""
+    import torch
+
+    import combine_moe_topk_amd as moe
+
+    moe.moe_topk_gate(cfg, lg, idx, wt, stream)
+    moe.moe_dispatch_layout(cfg, idx, lay, ws, stream)
+    T, K = w.T, w.K
+    seq = (torch.arange(K, dtype=torch.int32, device=x.device)[None, :] * T +
+           torch.arange(T, dtype=torch.int32, device=x.device)[:, None])
+    seq = seq.contiguous().view(-1)
+    orders = {"expert_major": lay.slot_pos, "sequential": seq}
+    for _ in range(args.warmup):
+        for sl in orders.values():
+            moe.moe_dispatch_pack(cfg, x, sl, send, stream)
+    res = {}
+    for name, sl in orders.items():
+        ms = _pct(_timed(lambda: moe.moe_dispatch_pack(cfg, x, sl, send,
+                                                       stream),
+                         args.steps, stream), 50)
+        res[name] = {"ms": ms,
+                     "gbps": kernel_bytes(w)["pack"] / (ms * 1e-3) / 1e9}
+    print(json.dumps({"path": "pack_orders", "workload": w.name,
+                      "steps": args.steps, "warmup": args.warmup, **res}),
+          flush=True)
     return 0
 
 

@@ -15,6 +15,11 @@ cycles it was busy with indexed accesses.
 assign`, or any run for the gate) and records the instructions one
 moe_assign_tasks call (its two kernels) or one gate launch issues, in total
 and per wave, in profiles/valu.json with the source hash.
+`pack_orders` reads a --kernel-trace run and --pmc runs of
+`bench.py --path pack_orders` and compares, per launch, the pack kernel with
+the expert-major slots against the same kernel with slot k*T + t: duration
+and the L2-to-memory write counters (requests, 64-byte requests, requests in
+flight per cycle, cycles stalled for DRAM credits, ...).
 `traffic` reads a FETCH_SIZE run and a WRITE_SIZE run of
 `bench.py --fused-only ... --copy-calib-mib MIB`, scales each counter by what
 it reads for the calibration copy (a device copy of MIB MiB, which reads and
@@ -235,6 +240,64 @@ def valu(db: str, workload: str, cmd: str, role: str = "assign") -> None:
         f.write("\n".join(md))
 
 
+def _pack_dispatches(rows, steps: int, warmup: int):
+    """Split the pack dispatches of a pack_orders run (dispatch order):
+    2*warmup warm-up launches, then `steps` expert-major, then `steps`
+    sequential.  rows: (dispatch_id, kernel_name, ...) tuples."""
+    ids = sorted({r[0] for r in rows if short(r[1]).startswith("pack")})
+    ids = ids[2 * warmup:2 * warmup + 2 * steps]
+    return {"expert_major": set(ids[:steps]), "sequential": set(ids[steps:])}
+
+
+def pack_orders(trace_db: str, pmc_dbs: list, workload: str, steps: int,
+                warmup: int, cmds: list) -> None:
+    c = sqlite3.connect(trace_db)
+    rows = list(c.execute("select dispatch_id, name, duration from kernels"))
+    split = _pack_dispatches(rows, steps, warmup)
+    dur = {o: [r[2] / 1000.0 for r in rows if r[0] in ids]
+           for o, ids in split.items()}
+    ctr = collections.defaultdict(lambda: collections.defaultdict(list))
+    for db in pmc_dbs:
+        c = sqlite3.connect(db)
+        crow = list(c.execute(
+            "select dispatch_id, kernel_name, counter_name, value from "
+            "counters_collection"))
+        sp = _pack_dispatches(crow, steps, warmup)
+        for did, _, name, v in crow:
+            for o, ids in sp.items():
+                if did in ids:
+                    ctr[o][name].append(v)
+    w = bench.mi.WORKLOADS[workload]
+    alg = bench.kernel_bytes(w)["pack"]
+    names = sorted({n for d in ctr.values() for n in d})
+    md = [f"# Pack destination order: {workload}\n", "Commands:\n"]
+    md += [f"    {c}" for c in cmds]
+    md += ["", "The pack kernel on the same buffers, once with the layout's "
+           "expert-major slots, once with slot k*T + t (every destination "
+           "row stream sequential).  Per launch, averaged over "
+           f"{steps} launches of each; algorithmic bytes {alg}.\n", "```",
+           f"{'':40s} {'expert_major':>16s} {'sequential':>16s}"]
+
+    def avg(v):
+        return sum(v) / len(v) if v else float("nan")
+    md.append(f"{'duration (us)':40s} {avg(dur['expert_major']):16.2f} "
+              f"{avg(dur['sequential']):16.2f}")
+    md.append(f"{'algorithmic GB/s':40s} "
+              f"{alg / avg(dur['expert_major']) / 1e3:16.1f} "
+              f"{alg / avg(dur['sequential']) / 1e3:16.1f}")
+    for n in names:
+        md.append(f"{n:40s} {avg(ctr['expert_major'][n]):16.0f} "
+                  f"{avg(ctr['sequential'][n]):16.0f}")
+    lvl, req = "TCC_EA0_WRREQ_LEVEL_sum", "TCC_EA0_WRREQ_sum"
+    if lvl in names and req in names:
+        md.append(f"{'write requests in flight / request':40s} "
+                  f"{avg(ctr['expert_major'][lvl]) / avg(ctr['expert_major'][req]):16.1f} "
+                  f"{avg(ctr['sequential'][lvl]) / avg(ctr['sequential'][req]):16.1f}")
+    md.append("```\n")
+    with open(os.path.join(PROFILES, f"pack_orders_{workload}.md"), "w") as f:
+        f.write("\n".join(md))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -251,6 +314,13 @@ def main() -> None:
     v.add_argument("--workload", default="deepseek_v3")
     v.add_argument("--cmd", required=True)
     v.add_argument("--role", default="assign", choices=("assign", "gate"))
+    o = sub.add_parser("pack_orders")
+    o.add_argument("trace_db")
+    o.add_argument("pmc_dbs", nargs="+")
+    o.add_argument("--workload", default="deepseek_v3")
+    o.add_argument("--steps", type=int, required=True)
+    o.add_argument("--warmup", type=int, required=True)
+    o.add_argument("--cmd", action="append", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("fetch_db")
     r.add_argument("write_db")
@@ -275,6 +345,9 @@ def main() -> None:
         lds(a.db, a.out, a.cmd)
     elif a.what == "valu":
         valu(a.db, a.workload, a.cmd, a.role)
+    elif a.what == "pack_orders":
+        pack_orders(a.trace_db, a.pmc_dbs, a.workload, a.steps, a.warmup,
+                    a.cmd)
     else:
         traffic(a.fetch_db, a.write_db, a.workload, a.calib_mib, a.cmd_fetch,
                 a.cmd_write, a.path, a.crossings, a.part_bytes, a.capacity,
