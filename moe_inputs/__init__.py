@@ -219,6 +219,47 @@ def logits_one_hot_experts(T: int, E: int, K: int, first: int = 0,
     return lg
 
 
+def logits_masked(T: int, E: int, seed: int = 0) -> np.ndarray:
+    """N(0, 1) logits with a share of each token's experts masked to -inf
+    (0, 50, 90 or 95 %, drawn per token), then one random expert of every
+    token set finite again, so each token keeps at least one finite logit
+    and may have fewer than K (its remaining picks are -inf ties)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lg = rng.standard_normal((T, E), dtype=np.float32)
+    share = rng.choice(np.array([0.0, 0.5, 0.9, 0.95]), size=T)
+    lg[rng.random((T, E)) < share[:, None]] = -np.inf
+    lg[np.arange(T), rng.integers(0, E, size=T)] = rng.standard_normal(
+        T, dtype=np.float32)
+    return lg
+
+
+def logits_floored(T: int, E: int, G: int, K: int, per_lane: int,
+                   seed: int = 0) -> np.ndarray:
+    """Logits that put a chosen number of candidates above a lane-maximum
+    threshold.  Lanes are the G residues of the expert index mod G, in rows
+    of 16; in each row kk = ceil(K / (G/16)) lanes are high: one holds a
+    single logit just above 10 (so it is the row's kk-th largest lane
+    maximum), each other holds `per_lane` logits in [10.5, 11); every other
+    logit is N(0, 1).  So (G/16) * (1 + (kk - 1) * per_lane) logits reach the
+    smallest such maximum.  Values are distinct with probability one (no
+    ties).  E must be a multiple of G."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lg = rng.standard_normal((T, E), dtype=np.float32)
+    C = E // G
+    rows = G // 16
+    kk = -(-K // rows)
+    for t in range(T):
+        for r in range(rows):
+            lanes = r * 16 + rng.choice(16, kk, replace=False)
+            j = int(rng.integers(C))
+            lg[t, lanes[0] + G * j] = np.float32(10.0 + rng.random() * 1e-3)
+            for sub in lanes[1:]:
+                js = rng.choice(C, per_lane, replace=False)
+                lg[t, sub + G * js] = (10.5 + 0.5 * rng.random(per_lane)
+                                       ).astype(np.float32)
+    return lg
+
+
 def random_x(T: int, H: int, dtype: str, seed: int = 0) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     x = rng.standard_normal((T, H), dtype=np.float32)

@@ -95,6 +95,58 @@ def test_gate_ties_many_tokens(name, make, E, K):
     check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
 
 
+def _gate_path_per_wave(lg, K, G):
+    """Which selection path each wave of the gate kernel takes (0: at most G
+    candidates a group, one LDS entry a lane; 1: at most 2G, two; 2: more,
+    the general path), from the kernel's threshold rule restated in numpy:
+    theta = min over the group's 16-lane rows of the row's
+    ceil(K/rows)-th largest lane maximum (lane sub holds experts sub + jG)."""
+    T, E = lg.shape
+    C = -(-E // G)
+    pad = np.full((T, G * C), -np.inf, np.float32)
+    pad[:, :E] = lg
+    key = pad.reshape(T, C, G).transpose(0, 2, 1)
+    lane_max = key.max(axis=2)
+    rows = G // 16
+    kk = -(-K // rows)
+    srt = -np.sort(-lane_max.reshape(T, rows, 16), axis=2)
+    theta = srt[:, :, kk - 1].min(axis=1)
+    valid = (np.arange(G)[:, None] + np.arange(C)[None, :] * G) < E
+    M = ((key >= theta[:, None, None]) & valid[None]).sum(axis=(1, 2))
+    Mw = M.reshape(-1, 64 // G).max(axis=1)
+    return np.where(Mw <= G, 0, np.where(Mw <= 2 * G, 1, 2))
+
+
+# Above 1024 tokens the gate takes G = 16 lanes a token for E = 256, K = 8
+# and G = 32 for E = 896, K = 16; the floored logits put every wave of the
+# launch on one chosen path, with distinct values (no ties).
+@pytest.mark.parametrize("E,K,G,per_lane,path",
+                         [(256, 8, 16, 2, 0), (256, 8, 16, 3, 1),
+                          (256, 8, 16, 5, 2), (896, 16, 32, 2, 0),
+                          (896, 16, 32, 3, 1), (896, 16, 32, 5, 2)])
+def test_gate_selection_paths(E, K, G, per_lane, path):
+    T = 2048
+    lg = mi.logits_floored(T, E, G, K, per_lane, seed=E + per_lane)
+    assert (_gate_path_per_wave(lg, K, G) == path).all()
+    w = mi.Workload("paths", T=T, H=8, E=E, K=K, R=1, N=1)
+    ref_idx, ref_w = oracle.gate(lg, K)
+    idx, wt = gpu_gate(w, lg)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
+@pytest.mark.parametrize("T", [300, 2000])  # 64 lanes a token, then 16-32
+@pytest.mark.parametrize("E,K", [(8, 2), (32, 8), (64, 16), (256, 8),
+                                 (896, 16), (1000, 32)])
+def test_gate_masked_logits(T, E, K):
+    # -inf logits (masked experts): a threshold of -inf sends a wave to the
+    # general path, and -inf picks go to the lowest indexes
+    lg = mi.logits_masked(T, E, seed=E + K + T)
+    w = mi.Workload("masked", T=T, H=8, E=E, K=K, R=1, N=1)
+    ref_idx, ref_w = oracle.gate(lg, K)
+    idx, wt = gpu_gate(w, lg)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
 def test_gate_no_renorm():
     w = mi.DEEPSEEK_V3.replace(T=1000)
     lg = mi.make_inputs(w, with_x=False)["logits"]
