@@ -249,6 +249,51 @@ def _pack_dispatches(rows, steps: int, warmup: int):
     return {"expert_major": set(ids[:steps]), "sequential": set(ids[steps:])}
 
 
+def _per_instance(pmc_dbs: list, steps: int, warmup: int):
+    """Per-instance TCC_EA0_WRREQ and TCC_EA0_WRREQ_LEVEL of the pack
+    dispatches (rows of rocpd_pmc_event), when a run collected them."""
+    import statistics
+    for db in pmc_dbs:
+        c = sqlite3.connect(db)
+        names = dict(c.execute("select id, name from rocpd_info_pmc"))
+        if not {"TCC_EA0_WRREQ", "TCC_EA0_WRREQ_LEVEL"} <= set(names.values()):
+            continue
+        ev = {}
+        rows = list(c.execute("select dispatch_id, kernel_name, counter_name, "
+                              "event_id from counters_collection"))
+        for did, _, cname, eid in rows:
+            ev[(did, cname)] = eid
+        split = _pack_dispatches(rows, steps, warmup)
+        vals = collections.defaultdict(list)
+        for eid, pid, v in c.execute("select event_id, pmc_id, value from "
+                                     "rocpd_pmc_event order by id"):
+            vals[(eid, names.get(pid))].append(v)
+        out = {}
+        for order, ids in split.items():
+            cvr, cvl, ml, n = [], [], [], 0
+            for did in ids:
+                r = vals[(ev[(did, "TCC_EA0_WRREQ")], "TCC_EA0_WRREQ")]
+                lv = vals[(ev[(did, "TCC_EA0_WRREQ_LEVEL")],
+                           "TCC_EA0_WRREQ_LEVEL")]
+                pairs = [(a, b) for a, b in zip(r, lv) if a > 0]
+                if len(pairs) < 2:
+                    continue
+                req = [a for a, _ in pairs]
+                lat = [b / a for a, b in pairs]
+                n = len(pairs)
+                cvr.append(statistics.pstdev(req) / statistics.mean(req))
+                cvl.append(statistics.pstdev(lat) / statistics.mean(lat))
+                ml.append(statistics.mean(lat))
+            if not cvr:
+                return None
+            out[order] = {"instances": n,
+                          "requests cv": statistics.mean(cvr),
+                          "in flight/request cv": statistics.mean(cvl),
+                          "in flight/request mean": statistics.mean(ml)}
+        return out
+    return None
+
+
 def pack_orders(trace_db: str, pmc_dbs: list, workload: str, steps: int,
                 warmup: int, cmds: list) -> None:
     c = sqlite3.connect(trace_db)
@@ -294,6 +339,18 @@ def pack_orders(trace_db: str, pmc_dbs: list, workload: str, steps: int,
                   f"{avg(ctr['expert_major'][lvl]) / avg(ctr['expert_major'][req]):16.1f} "
                   f"{avg(ctr['sequential'][lvl]) / avg(ctr['sequential'][req]):16.1f}")
     md.append("```\n")
+    inst = _per_instance(pmc_dbs, steps, warmup)
+    if inst:
+        md += ["Per L2 channel (TCC instance; counters without _sum keep one "
+               "value per instance): the spread of the write requests and of "
+               "the requests in flight per request over the instances, as a "
+               "coefficient of variation, averaged over the launches.\n",
+               "```", f"{'':40s} {'expert_major':>16s} {'sequential':>16s}"]
+        for k in ("instances", "requests cv", "in flight/request cv",
+                  "in flight/request mean"):
+            md.append(f"{k:40s} {inst['expert_major'][k]:16.3f} "
+                      f"{inst['sequential'][k]:16.3f}")
+        md.append("```\n")
     with open(os.path.join(PROFILES, f"pack_orders_{workload}.md"), "w") as f:
         f.write("\n".join(md))
 
