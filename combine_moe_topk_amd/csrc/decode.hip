@@ -25,9 +25,9 @@
 //     token t wrote, so the workgroup that packs a token's rows combines
 //     them: after a workgroup barrier its threads read the rows back from
 //     send (never from x) and sum them.
-// A workgroup owns (token t, part p of its row); workgroup (0, 0) also
-// writes the batch-wide outputs (counts and offsets), parts p = 0 write the
-// token's own layout outputs.
+// Workgroup 0 writes the batch-wide outputs (counts, offsets, node masks
+// and node slots); workgroup 1 + t*P + p owns part p of token t's row, and
+// parts p = 0 write the token's own layout outputs.
 #include <algorithm>
 
 #include "moe_internal.h"
