@@ -592,10 +592,32 @@ size_t rank_lds_bytes(const moe_cfg &c, int w) {
   return (size_t)w * (c.E + c.N) * 8 + (size_t)(c.E + c.N + 18) * 4;
 }
 
+// Default tokens per layout tile.  More tiles spread the count and rank
+// kernels over more CUs; each tile also adds one table row to the column
+// scan and one more workgroup to drain.  Measured on the model shapes, the
+// layout is fastest near 128 tiles, so the tile starts at 256 tokens and
+// halves (down to 64) while it leaves fewer than 91 tiles, the count nearest
+// 128 on a log scale.  A smaller tile is taken only while the table stays
+// within 256 KiB, which keeps the workspace of wide configurations small.
+// Up to 256 tokens the single tile stays: one workgroup then does the whole
+// layout.
+static int default_layout_tile(const moe_cfg &c, int cols) {
+  int tile = kDefaultLayoutTile;
+  if (c.T <= tile) return tile;
+  while (tile > kMinDefaultLayoutTile) {
+    if ((c.T + tile - 1) / tile >= kLayoutTileCountFloor) break;
+    const int half = tile / 2;
+    const size_t rows = (size_t)(c.T + half - 1) / half + 1;
+    if (rows * cols * 4 > kLayoutShrinkTableMax) break;
+    tile = half;
+  }
+  return tile;
+}
+
 LayoutGeom layout_geom(const moe_cfg &c) {
   LayoutGeom g{};
   g.cols = c.E + c.R + c.N;
-  const int want = c.layout_tile ? c.layout_tile : kDefaultLayoutTile;
+  const int want = c.layout_tile ? c.layout_tile : default_layout_tile(c, g.cols);
   int w = want / kWave;
   // count kernel: W*cols*8 bytes; rank kernel: W*(E+N)*8 + (E+N+18)*4
   while (w > 1 && ((size_t)w * g.cols * 8 > (size_t)kLdsBudget ||

@@ -13,7 +13,10 @@ namespace moe {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr size_t kWsHeader = 256;    // workspace header: error word + pad
 constexpr int kLdsBudget = 65536;    // bytes of LDS a layout workgroup may use
-constexpr int kDefaultLayoutTile = 256;
+constexpr int kDefaultLayoutTile = 256;    // largest default layout tile
+constexpr int kMinDefaultLayoutTile = 64;  // smallest default layout tile
+constexpr int kLayoutTileCountFloor = 91;  // default tile halves below this
+constexpr size_t kLayoutShrinkTableMax = 256 << 10;  // bytes
 constexpr int kMaxLevels = MOE_MAX_LEVELS;  // capacity / bucket levels
 
 // 16-byte vector used for every row copy (one global_load/store_dwordx4).

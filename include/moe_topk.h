@@ -89,9 +89,12 @@ typedef struct moe_cfg {
   int32_t x_dtype;     /* MOE_F32 or MOE_BF16: x, send and y rows             */
   int32_t out_dtype;   /* MOE_F32 or MOE_BF16: combine output                 */
   uint32_t flags;      /* MOE_F_* bits                                        */
-  int32_t layout_tile; /* tokens per layout workgroup: 0 (default 256) or one
-                          of 64, 128, 256, 512, 1024.  Results do not depend
-                          on it; the workspace size does.                     */
+  int32_t layout_tile; /* tokens per layout workgroup: 64, 128, 256, 512 or
+                          1024, or 0 for the default: 256 when T <= 256,
+                          else 256 halved (down to 64) while that leaves
+                          fewer than 91 tiles and a table of at most 256 KiB
+                          ((tiles + 1) * (E + R + N) int32).  Results do not
+                          depend on it; the workspace size does.              */
 } moe_cfg;
 
 /* Outputs of the dispatch layout (device pointers, caller-allocated).

@@ -88,15 +88,28 @@ def test_validate_rejects_bad_tile_flags_dtype():
 
 
 def test_workspace_bytes():
-    c = cfg()
-    n = moe.moe_workspace_bytes(c)
-    # 256-byte header + (ceil(T/256) + 1) rows of (E + R + N) int32, rounded
-    rows = 16384 // 256 + 1
-    assert n == 256 + ((rows * (256 + 64 + 8) * 4 + 255) // 256) * 256
+    def ws(T, tile, cols=256 + 64 + 8):
+        # 256-byte header + (ceil(T/tile) + 1) rows of (E + R + N) int32
+        rows = -(-T // tile) + 1
+        return 256 + ((rows * cols * 4 + 255) // 256) * 256
+
+    n = moe.moe_workspace_bytes(cfg(layout_tile=256))
+    assert n == ws(16384, 256)
     assert n % 256 == 0
     assert moe.moe_workspace_bytes(cfg(T=-1)) == 0
     # smaller tiles need more rows; results do not depend on the tile
     assert moe.moe_workspace_bytes(cfg(layout_tile=64)) > n
+    # default tile: 256 halved (to 64 at least) while under 91 tiles and a
+    # table of at most 256 KiB; one 256-token tile up to 256 tokens
+    assert moe.moe_workspace_bytes(cfg()) == ws(16384, 128)
+    assert moe.moe_workspace_bytes(cfg(T=32768)) == ws(32768, 256)
+    assert moe.moe_workspace_bytes(cfg(T=8192)) == ws(8192, 64)
+    assert moe.moe_workspace_bytes(cfg(T=200)) == ws(200, 256)
+    assert moe.moe_workspace_bytes(cfg(T=300)) == ws(300, 64)
+    # E = 896, R = 128, N = 16 at 8192 tokens: tile 128 would need a
+    # 65-row table of 1040 columns (> 256 KiB), so 256 stays
+    wide = cfg(T=8192, E=896, K=16, R=128, N=16)
+    assert moe.moe_workspace_bytes(wide) == ws(8192, 256, 896 + 128 + 16)
     # empty input still needs the header and the offsets row
     assert moe.moe_workspace_bytes(cfg(T=0)) > 256
 
