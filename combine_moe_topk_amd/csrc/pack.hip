@@ -84,12 +84,26 @@ constexpr int kPieceVP = 2;  // 16-byte vectors per lane in a piece
 constexpr int kPieceG = 2;   // destinations per wave
 constexpr size_t kPieceMinBytes = size_t(1) << 30;  // destination rows
 
+// Hardware workgroup b runs on XCD b % 8 (the dispatcher deals workgroups
+// out to the XCDs in turn).  When a piece's NG destination groups span
+// B = NG / 4 workgroups, the workgroups are renumbered in groups of 8 B so
+// that the B sharing a piece of x run on one XCD and share its L2, rather
+// than each of B XCDs fetching the piece from memory.  The last, partial
+// group keeps its numbers.
+__device__ __forceinline__ int piece_block(int b, int B, int nb) {
+  const int span = 8 * B;
+  if (B <= 1 || b >= nb - nb % span) return b;
+  const int r = b % span;
+  return b - r + B * (r % 8) + r / 8;
+}
+
 __global__ __launch_bounds__(256) void pack_piece_kernel(
     const u32x4 *__restrict__ x, const int32_t *__restrict__ slots,
     u32x4 *__restrict__ send, int W, int V, int P, int NG, int rows, int n) {
   const int lane = threadIdx.x % kWave;
+  const int B = NG % 4 == 0 ? NG / 4 : 1;
   // wave index made wave-uniform so the index arithmetic runs on the SALU
-  const int g = blockIdx.x * (256 / kWave) +
+  const int g = piece_block(blockIdx.x, B, gridDim.x) * (256 / kWave) +
                 __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (g >= n) return;  // n = T*P*NG waves of work
   const int q = g % NG;  // NG = ceil(W / kPieceG) destination groups
