@@ -86,13 +86,23 @@ hipError_t launch_fused(const moe_cfg &c, const void *x, const float *logits,
                         const float *expert_scale, int32_t *topk_idx,
                         float *topk_w, const moe_layout &lay, void *send,
                         void *out, void *ws, hipStream_t stream) {
-  hipError_t e = launch_gate(c, logits, topk_idx, topk_w, stream);
-  if (e != hipSuccess) return e;
-  // a decode-sized batch: layout, pack and combine in one launch
-  if (decode_ok(c))
-    return launch_decode(c, x, topk_idx, topk_w, expert_scale, lay, send, out,
-                         stream);
-  e = launch_layout(c, topk_idx, lay, ws, stream);
+  hipError_t e;
+  if (!decode_ok(c) && gate_count_ok(c)) {
+    // the gate also writes the layout's per-tile counts: one launch fewer,
+    // and the ids are not read back for counting
+    e = launch_gate_count(c, logits, topk_idx, topk_w, lay.node_mask, ws,
+                          stream);
+    if (e == hipSuccess)
+      e = launch_layout_after_count(c, topk_idx, lay, ws, stream);
+  } else {
+    e = launch_gate(c, logits, topk_idx, topk_w, stream);
+    if (e != hipSuccess) return e;
+    // a decode-sized batch: layout, pack and combine in one launch
+    if (decode_ok(c))
+      return launch_decode(c, x, topk_idx, topk_w, expert_scale, lay, send,
+                           out, stream);
+    e = launch_layout(c, topk_idx, lay, ws, stream);
+  }
   if (e == hipSuccess) e = launch_pack(c, x, lay.slot_pos, send, stream);
   if (e == hipSuccess)
     e = launch_combine(c, send, lay.slot_pos, topk_w, topk_idx, expert_scale,

@@ -1,6 +1,6 @@
-// Device code of the top-K gate, shared by the gate kernel and the fused
-// decode kernel (which runs the gate of its own token before a grid-wide
-// barrier).  Not part of the ABI.
+// Device code of the top-K gate, shared by the gate kernel and the kernel
+// that runs the gate and the layout's per-tile counts in one launch.  Not
+// part of the ABI.
 //
 // "Efficient and portable mixture-of-experts communication", section
 // "Introdución": the router yields a distribution over experts, the top-K

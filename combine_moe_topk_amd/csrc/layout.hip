@@ -634,42 +634,18 @@ LayoutGeom layout_geom(const moe_cfg &c) {
 
 namespace {
 
+// The scan and rank launches, once the count table's rows [0, nblocks) and
+// node_mask hold the per-tile counts (from layout_count_kernel, or from the
+// gate's fused count pass).
 template <int KM>
-hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
-                            const moe_layout &lay, void *ws,
-                            hipStream_t stream) {
+hipError_t launch_layout_tail(const moe_cfg &c, const int32_t *topk_idx,
+                              const moe_layout &lay, void *ws,
+                              hipStream_t stream) {
   const LayoutGeom g = layout_geom(c);
-  int32_t *err = (int32_t *)ws;
   int32_t *table = (int32_t *)((char *)ws + kWsHeader);
   const int per_rank = c.E / c.R;
-  const uint32_t m_rank = div_magic(per_rank);
   const uint32_t m_node = div_magic(c.E / c.N);
   const int threads = g.tile_tokens;
-
-  if (g.nblocks == 1) {
-    // every token in one tile: one workgroup does the whole layout
-    const int P = (c.T + kWave - 1) / kWave;
-    const size_t lds = (size_t)P * g.cols * 12 +
-                       (size_t)(g.cols + c.E + 1 + c.N + 1) * 4;
-    if (lds <= (size_t)kLdsBudget) {
-      hipLaunchKernelGGL((layout_block_kernel<KM>), dim3(1), dim3(1024),
-                         lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
-                         per_rank, m_rank, m_node, lay.expert_count,
-                         lay.expert_off, lay.rank_count, lay.rank_off,
-                         lay.rank_token_count, lay.node_mask, lay.node_count,
-                         lay.node_off, lay.node_slot, lay.slot_pos,
-                         lay.row_src, err);
-      return hipGetLastError();
-    }
-  }
-  if (g.nblocks > 0) {
-    const size_t lds = (size_t)g.tile_waves * g.cols * 8;
-    hipLaunchKernelGGL(layout_count_kernel<KM>, dim3(g.nblocks), dim3(threads),
-                       lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
-                       m_rank, m_node, lay.node_mask, table, err);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const LayoutOut lo{lay.expert_count, lay.expert_off, lay.rank_count,
                      lay.rank_off, lay.rank_token_count, lay.node_count,
                      lay.node_off};
@@ -708,6 +684,45 @@ hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
   return hipGetLastError();
 }
 
+template <int KM>
+hipError_t launch_layout_km(const moe_cfg &c, const int32_t *topk_idx,
+                            const moe_layout &lay, void *ws,
+                            hipStream_t stream) {
+  const LayoutGeom g = layout_geom(c);
+  int32_t *err = (int32_t *)ws;
+  int32_t *table = (int32_t *)((char *)ws + kWsHeader);
+  const int per_rank = c.E / c.R;
+  const uint32_t m_rank = div_magic(per_rank);
+  const uint32_t m_node = div_magic(c.E / c.N);
+  const int threads = g.tile_tokens;
+
+  if (g.nblocks == 1) {
+    // every token in one tile: one workgroup does the whole layout
+    const int P = (c.T + kWave - 1) / kWave;
+    const size_t lds = (size_t)P * g.cols * 12 +
+                       (size_t)(g.cols + c.E + 1 + c.N + 1) * 4;
+    if (lds <= (size_t)kLdsBudget) {
+      hipLaunchKernelGGL((layout_block_kernel<KM>), dim3(1), dim3(1024),
+                         lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
+                         per_rank, m_rank, m_node, lay.expert_count,
+                         lay.expert_off, lay.rank_count, lay.rank_off,
+                         lay.rank_token_count, lay.node_mask, lay.node_count,
+                         lay.node_off, lay.node_slot, lay.slot_pos,
+                         lay.row_src, err);
+      return hipGetLastError();
+    }
+  }
+  if (g.nblocks > 0) {
+    const size_t lds = (size_t)g.tile_waves * g.cols * 8;
+    hipLaunchKernelGGL(layout_count_kernel<KM>, dim3(g.nblocks), dim3(threads),
+                       lds, stream, topk_idx, c.T, c.K, c.E, c.R, c.N,
+                       m_rank, m_node, lay.node_mask, table, err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_layout_tail<KM>(c, topk_idx, lay, ws, stream);
+}
+
 }  // namespace
 
 hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
@@ -717,6 +732,16 @@ hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
   if (c.K <= 8) return launch_layout_km<8>(c, topk_idx, lay, ws, stream);
   if (c.K <= 16) return launch_layout_km<16>(c, topk_idx, lay, ws, stream);
   return launch_layout_km<32>(c, topk_idx, lay, ws, stream);  // K <= 32
+}
+
+hipError_t launch_layout_after_count(const moe_cfg &c,
+                                     const int32_t *topk_idx,
+                                     const moe_layout &lay, void *ws,
+                                     hipStream_t stream) {
+  if (c.K <= 4) return launch_layout_tail<4>(c, topk_idx, lay, ws, stream);
+  if (c.K <= 8) return launch_layout_tail<8>(c, topk_idx, lay, ws, stream);
+  if (c.K <= 16) return launch_layout_tail<16>(c, topk_idx, lay, ws, stream);
+  return launch_layout_tail<32>(c, topk_idx, lay, ws, stream);
 }
 
 }  // namespace moe

@@ -68,6 +68,25 @@ hipError_t launch_gate(const moe_cfg &c, const float *logits,
 hipError_t launch_layout(const moe_cfg &c, const int32_t *topk_idx,
                          const moe_layout &lay, void *ws, hipStream_t stream);
 
+// The layout's scan and rank launches alone (layout.hip), for when the
+// count table rows [0, nblocks) and node_mask already hold the per-tile
+// counts that its count launch would write.
+hipError_t launch_layout_after_count(const moe_cfg &c,
+                                     const int32_t *topk_idx,
+                                     const moe_layout &lay, void *ws,
+                                     hipStream_t stream);
+
+// The gate and the layout's count launch as one launch (gate.hip): the
+// gate's picks plus the count table rows and node_mask, as launch_gate and
+// then the count launch of launch_layout would leave them.  gate_count_ok:
+// the gate takes 16 lanes a token and the layout has more than one tile of
+// at most 128 tokens (a workgroup runs the gate of 64 tokens at a time).
+bool gate_count_ok(const moe_cfg &c);
+hipError_t launch_gate_count(const moe_cfg &c, const float *logits,
+                             int32_t *topk_idx, float *topk_w,
+                             uint64_t *node_mask, void *ws,
+                             hipStream_t stream);
+
 // send-style copy: dst[slots[t*W + w]] = x[t] for w < W (W <= 64), entries
 // outside [0, rows) skipped; row_bytes a multiple of 16.
 hipError_t launch_pack_rows(const void *x, const int32_t *slots, int W,

@@ -457,6 +457,76 @@ def test_fused_edge_shapes(T, H, E, K, R, N, xdt, odt):
               term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef), odt)
 
 
+# Past 1024 tokens, when the gate takes 16 lanes a token (E <= 512, K <= 8)
+# and the layout tile holds 64 tokens (the default tile for these sizes),
+# the fused call runs the gate and the layout's count pass as one launch:
+# ragged tails (a last tile of one token, partial last waves), padding keys
+# (E not a multiple of 16), masked logits, no optional outputs, and one
+# 128-token tile, which takes the separate launches.  Checked against the
+# oracle and bit for bit against the separate gate, layout, pack and
+# combine calls.
+GATE_COUNT_SHAPES = [
+    # T, H, E, K, R, N, tile, masked, optional
+    (1025, 64, 8, 2, 8, 1, 64, False, True),
+    (1500, 128, 128, 8, 64, 8, 0, False, True),
+    (2049, 64, 256, 8, 64, 8, 64, False, True),
+    (3000, 64, 128, 8, 64, 8, 0, True, True),
+    (4133, 32, 512, 8, 128, 16, 64, True, False),
+    (1100, 72, 48, 6, 8, 4, 0, False, True),
+    (2100, 64, 256, 8, 64, 8, 128, False, True),
+]
+
+
+@pytest.mark.parametrize("case", GATE_COUNT_SHAPES,
+                         ids=lambda c: f"T{c[0]}-E{c[2]}-K{c[3]}-tile{c[6]}")
+def test_fused_gate_count(case):
+    T, H, E, K, R, N, tile, masked, optional = case
+    w = mi.Workload("gate_count", T=T, H=H, E=E, K=K, R=R, N=N,
+                    expert="mod8")
+    d = mi.make_inputs(w)
+    if masked:
+        d["logits"] = mi.logits_masked(T, E, seed=T + E)
+    ref = oracle.dispatch_combine(d["x"], d["logits"], K, R, N,
+                                  d["expert_scale"], w.out_dtype)
+    cfg = cfg_of(w, tile)
+    x, lg = dev(d["x"]), dev(d["logits"])
+    sc = None if d["expert_scale"] is None else dev(d["expert_scale"])
+    idx = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    wt = torch.empty(T * K, dtype=torch.float32, device="cuda")
+    lay = moe.alloc_layout(cfg, optional=optional)
+    send = torch.empty((T * K, H), dtype=row_dtype(w), device="cuda")
+    out = torch.empty((T, H), dtype=out_dtype(w), device="cuda")
+    ws = moe.alloc_workspace(cfg)
+    moe.moe_dispatch_combine(cfg, x, lg, sc, idx, wt, lay, send, out, ws)
+    assert moe.moe_read_device_error(ws) == 0
+    res = layout_to_host(lay, T, K, N)
+    res.update(topk_idx=host(idx).reshape(T, K), topk_w=host(wt).reshape(T, K))
+    check_gate(res, ref["topk_idx"], ref["topk_w"])
+    check_layout(res, ref)
+    np.testing.assert_array_equal(host(send), ref["send"])
+    coef = ref["topk_w"].astype(np.float64)
+    if d["expert_scale"] is not None:
+        coef = coef * d["expert_scale"][ref["topk_idx"]]
+    check_out(host(out), ref["out_exact"],
+              term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef),
+              w.out_dtype)
+    # the same bits as the gate, layout, pack and combine calls one by one
+    idx2, wt2 = torch.empty_like(idx), torch.empty_like(wt)
+    moe.moe_topk_gate(cfg, lg, idx2, wt2)
+    assert torch.equal(idx, idx2) and torch.equal(wt, wt2)
+    ws2 = moe.alloc_workspace(cfg)
+    lay2 = moe.alloc_layout(cfg, optional=optional)
+    send2, out2 = torch.empty_like(send), torch.empty_like(out)
+    moe.moe_dispatch_layout(cfg, idx2, lay2, ws2)
+    moe.moe_dispatch_pack(cfg, x, lay2.slot_pos, send2)
+    moe.moe_combine(cfg, send2, lay2.slot_pos, wt2, idx2, sc, out2)
+    for name in LAYOUT_KEYS:
+        a, b = getattr(lay, name), getattr(lay2, name)
+        if a is not None:
+            assert torch.equal(a, b), name
+    assert torch.equal(send, send2) and torch.equal(out, out2)
+
+
 # Batches of up to 1024 tokens (T*K <= 4096) take the one-launch decode
 # step after the gate: ragged and tiny batches, K = 1 and K = E, many nodes,
 # E = 1024, fp32 rows and outputs, no expert scale, no optional outputs.
