@@ -367,6 +367,8 @@ __device__ void offsets_from_totals(int32_t *ebase, int32_t *nbase, int E,
 // each column.
 // TOTALS false: the tail row already holds the global offsets (the
 // one-workgroup scan wrote them and the batch-wide outputs).
+constexpr int kRankRowRegs = 8;  // table values a thread loads at once
+
 template <int KM, bool TOTALS>
 __global__ __launch_bounds__(1024) void layout_rank_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
@@ -389,13 +391,39 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   for (int i = threadIdx.x; i < W * cr; i += blockDim.x) bm[i] = 0;
   const int32_t *tile = table + (size_t)blockIdx.x * cols;
   const int32_t *tail = table + (size_t)gridDim.x * cols;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) ebase[e] = tail[e];
-  for (int n = threadIdx.x; n < N; n += blockDim.x) nbase[n] = tail[E + R + n];
+  // The expert and node columns (value j < E + N: column j, or E + R + j - E
+  // for a node) of the tail row and of the tile's row.  The first
+  // kRankRowRegs * B of each are loaded together, with the ids, into
+  // registers (a loop of loads and LDS stores waits for each load in turn:
+  // that was 1.4 us for DeepSeek-V3 and 3.3 us for Kimi K2 before the
+  // offsets could start, and as much again for the tile's row); the rest,
+  // for very wide tables only, in a loop.
+  const int B = blockDim.x;
+  int tl[kRankRowRegs], tv[kRankRowRegs];
+#pragma unroll
+  for (int u = 0; u < kRankRowRegs; ++u) {
+    const int j = u * B + threadIdx.x;
+    const int col = j < E ? j : j + R;
+    tl[u] = j < cr ? tail[col] : 0;
+    tv[u] = j < cr ? tile[col] : 0;
+  }
+#pragma unroll
+  for (int u = 0; u < kRankRowRegs; ++u) {
+    const int j = u * B + threadIdx.x;
+    if (j < cr) ebase[j < E ? j : j + 1] = tl[u];  // nbase = ebase + E + 1
+  }
+  for (int j = kRankRowRegs * B + threadIdx.x; j < cr; j += B)
+    ebase[j < E ? j : j + 1] = tail[j < E ? j : j + R];
   __syncthreads();
   if constexpr (TOTALS) offsets_from_totals(ebase, nbase, E, R, N, per_rank,
                                             tail, lo, wsum);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) ebase[e] += tile[e];
-  for (int n = threadIdx.x; n < N; n += blockDim.x) nbase[n] += tile[E + R + n];
+#pragma unroll
+  for (int u = 0; u < kRankRowRegs; ++u) {
+    const int j = u * B + threadIdx.x;
+    if (j < cr) ebase[j < E ? j : j + 1] += tv[u];
+  }
+  for (int j = kRankRowRegs * B + threadIdx.x; j < cr; j += B)
+    ebase[j < E ? j : j + 1] += tile[j < E ? j : j + R];
   __syncthreads();
 
   const uint64_t bit = 1ull << lane;
