@@ -231,6 +231,9 @@ __global__ __launch_bounds__(1024) void layout_scan_cols_kernel(
   const int r0 = min(nblocks, ch * per);
   const int r1 = min(nblocks, r0 + per);
   int32_t *col = table + c;
+  // the chunk's first 8 rows stay in registers for the prefix pass (up to
+  // 128 tiles that is the whole chunk); later rows are loaded again
+  int v0[8];
   int sum = 0;
   for (int r = r0; r < r1; r += 8) {
     int v[8];
@@ -240,6 +243,10 @@ __global__ __launch_bounds__(1024) void layout_scan_cols_kernel(
     for (int q = 0; q < 8; ++q) asm volatile("" : "+v"(v[q]));
 #pragma unroll
     for (int q = 0; q < 8; ++q) sum += r + q < r1 ? v[q] : 0;
+    if (r == r0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v0[q] = v[q];
+    }
   }
   part[ch][cl] = sum;
   __syncthreads();
@@ -249,10 +256,16 @@ __global__ __launch_bounds__(1024) void layout_scan_cols_kernel(
   if (ch == kScanChunks - 1) col[(size_t)nblocks * cols] = run + sum;
   for (int r = r0; r < r1; r += 8) {
     int v[8];
+    if (r == r0) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = col[(size_t)min(r + q, r1 - 1) * cols];
+      for (int q = 0; q < 8; ++q) v[q] = v0[q];
+    } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) asm volatile("" : "+v"(v[q]));
+      for (int q = 0; q < 8; ++q)
+        v[q] = col[(size_t)min(r + q, r1 - 1) * cols];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) asm volatile("" : "+v"(v[q]));
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (r + q < r1) {
