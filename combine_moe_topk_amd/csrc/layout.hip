@@ -309,14 +309,12 @@ __device__ void scan_inplace(int32_t *a, int n, int32_t *wsum) {
   const int w = threadIdx.x / kWave;
   if (lane == kWave - 1) wsum[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int v = 0; v < B / kWave; ++v) {
-      const int s = wsum[v];
-      wsum[v] = run;
-      run += s;
-    }
-    a[n] = run;
+  if (w == 0) {  // wave 0 scans the wave sums (at most 16)
+    const int nw = B / kWave;
+    const int s = lane < nw ? wsum[lane] : 0;
+    const int si = wave_inclusive_scan(s);
+    if (lane < nw) wsum[lane] = si - s;
+    if (lane == nw - 1) a[n] = si;
   }
   __syncthreads();
   int run = wsum[w] + inc - local;
@@ -340,16 +338,16 @@ __device__ void offsets_from_totals(int32_t *ebase, int32_t *nbase, int E,
                                     int R, int N, int per_rank,
                                     const int32_t *tail, const LayoutOut &lo,
                                     int32_t *wsum) {
-  scan_inplace(ebase, E, wsum);  // ends with a barrier
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int n = 0; n < N; ++n) {
-      const int v = nbase[n];
-      nbase[n] = run;
-      run += v;
-    }
-    nbase[N] = run;
+  // wave 0 scans the node totals (N <= 64) in registers while the
+  // workgroup scans the expert totals
+  int nv = 0, ni = 0;
+  if (threadIdx.x < kWave) {
+    nv = (int)threadIdx.x < N ? nbase[threadIdx.x] : 0;
+    ni = wave_inclusive_scan(nv);
   }
+  scan_inplace(ebase, E, wsum);  // ends with a barrier
+  if ((int)threadIdx.x < N) nbase[threadIdx.x] = ni - nv;
+  if ((int)threadIdx.x == N - 1) nbase[N] = ni;
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
