@@ -1,5 +1,7 @@
-// Top-K gate kernel for gfx950: one group of G lanes per token; the
-// selection itself (threshold, compaction, rank) is in gate_core.h.
+// Top-K gate kernels for gfx950: one group of G lanes per token; the
+// selection itself (threshold, compaction, rank) is in gate_core.h.  The
+// gate kernel writes the picks; the gate-count kernel, for the fused call,
+// also writes the dispatch layout's per-tile counts in the same launch.
 //
 // "Efficient and portable mixture-of-experts communication", section
 // "Introdución": the router yields a distribution over experts, the top-K

@@ -24,10 +24,14 @@
 // one workgroup does everything (layout_block_kernel).  Otherwise three
 // launches:
 //   count: per-tile column counts (experts | ranks | nodes) + node masks
-//   scan : one workgroup turns the count table into per-tile exclusive
-//          prefixes, totals, expert/rank/node offsets
+//   scan : the count table to per-tile exclusive prefixes and column totals
+//          (one workgroup up to 32 tiles, which also writes the offsets;
+//          else column-parallel, and the rank workgroups derive the
+//          offsets from the totals)
 //   rank : rebuilds the tile bitmaps and writes slot_pos, row_src, node_slot
-// The count table lives in the caller's workspace: nblocks x (E + R + N).
+// In the fused call the gate can write the counts itself (gate.hip), and
+// only scan and rank run here.  The count table lives in the caller's
+// workspace: (nblocks + 1) x (E + R + N), the last row for the totals.
 #include <algorithm>
 
 #include "moe_internal.h"
