@@ -37,9 +37,10 @@ def _host(w, b):
 @pytest.mark.gpu
 def test_noalloc_matches_fused_call_with_shrinking_inputs():
     require_gpu()
-    cases = [mi.DEEPSEEK_V3.replace(T=5000, H=512),   # 20 layout tiles
+    cases = [mi.DEEPSEEK_V3.replace(T=5000, H=512),   # 79 tiles; the gate
+                                                      # writes the counts
              mi.KIMI.replace(T=2000, H=256),          # larger E, fewer tokens
-             mi.DEEPSEEK_V3_DECODE]                   # one-workgroup layout
+             mi.DEEPSEEK_V3_DECODE]                   # the decode launch
     inputs = [mi.make_inputs(w) for w in cases]
     dev_in = [(dev(d["x"]), dev(d["logits"]), dev(d["expert_scale"]))
               for d in inputs]
