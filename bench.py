@@ -245,6 +245,38 @@ def _timed(fn, n, stream, before=None):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def _timed_b2b(fn, n, stream) -> float:
+    """Mean duration (ms) of n calls of fn enqueued back to back between
+    one pair of HIP events: the GPU's time per call whenever the host
+    enqueues faster than the GPU runs them."""
+    import torch
+
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def _gate_split(gate, step, n, stream):
+    """(gate ms, step ms) on the GPU for a decode-sized step.  A gate call
+    alone is enqueued about as slowly as the GPU runs it, so timing it
+    back to back measures the host; instead the gate is timed as the extra
+    time of back-to-back [gate, step] pairs over back-to-back steps, which
+    the GPU paces."""
+    def both():
+        gate()
+        step()
+    alone = _timed_b2b(step, n, stream)
+    pair = _timed_b2b(both, n, stream)
+    return pair - alone, alone
+
+
 def sequential_bounds(w, dev, stream, n=20) -> dict:
     """The pack and the combine on the same buffers and bytes as the step,
     with the slot table k*T + t instead of the expert-major permutation: every
@@ -344,17 +376,21 @@ def config_line(w, dev, n=20) -> dict:
             "frac_of_peak": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "frac_of_peak_cold_clean":
                 alg / (_pct(clean, 50) * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-    gate = _pct(_timed(lambda: moe.moe_topk_gate(cfg, lg, idx, wt, stream),
-                       n, stream), 50)
     if w.T <= DECODE_MAX_T and w.T * w.K <= DECODE_MAX_TK:
-        # gate, then one decode kernel: its time is the step minus the gate
-        dk = ms - gate
+        # gate, then one decode kernel: its time is the step less the gate
+        gate, b2b = _gate_split(
+            lambda: moe.moe_topk_gate(cfg, lg, idx, wt, stream), step, 4 * n,
+            stream)
+        dk = b2b - gate
         by = alg - w.T * (4 * w.E + 8 * w.K)  # less the gate's own bytes
+        line["ms_back_to_back"] = b2b
         line["dominant"] = {"kernel": "decode (layout+pack+combine)",
                             "ms": dk, "gbps": by / (dk * 1e-3) / 1e9,
                             "frac": by / (dk * 1e-3) / 1e9 / HBM_PEAK_GBPS}
         line["gate_ms"] = gate
     else:
+        gate = _pct(_timed(lambda: moe.moe_topk_gate(cfg, lg, idx, wt,
+                                                     stream), n, stream), 50)
         lay_ms = _pct(_timed(lambda: moe.moe_dispatch_layout(
             cfg, idx, lay, ws, stream), n, stream), 50)
         pk, cb = [], []
@@ -632,7 +668,31 @@ def main() -> int:
                 "frac_of_peak": gbps / HBM_PEAK_GBPS},
     }
 
-    if not args.fused_only:
+    decode_sized = w.T <= DECODE_MAX_T and w.T * w.K <= DECODE_MAX_TK
+    if not args.fused_only and decode_sized:
+        # ---- decode-sized: the gate, then one decode kernel ----------------
+        # The fused call runs layout, pack and combine as one kernel here, so
+        # the separate calls would time other kernels (and, at a few
+        # microseconds each, the host's launch gaps).  The decode kernel's
+        # time is the fused step less the gate, as in extras.configs.
+        gate, b2b = _gate_split(
+            lambda: moe.moe_topk_gate(cfg, lg, idx, wt, stream), step,
+            max(args.steps, 50), stream)
+        dk = b2b - gate
+        by = alg - w.T * (4 * w.E + 8 * w.K)  # less the gate's own bytes
+        result["steps_ms"] = {"gate": gate, "decode": dk}
+        result["roofline"] = {
+            "kernel": "decode", "bound": "hbm",
+            "achieved": by / (dk * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": by / (dk * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "traffic": None,
+            "traffic_source": traffic_source("decode", w.name, None),
+            "alg_bytes_per_launch": by, "launch_ms": dk,
+            "timing": "back-to-back fused steps less the gate, the gate "
+                      "timed as the extra time of back-to-back [gate, "
+                      "step] pairs",
+        }
+    elif not args.fused_only:
         # ---- per-kernel durations inside a real step ------------------------
         # The four calls below launch exactly the kernels of one fused step,
         # in the same order on the same stream; HIP events between them give
