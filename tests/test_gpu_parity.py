@@ -527,6 +527,41 @@ def test_fused_gate_count(case):
     assert torch.equal(send, send2) and torch.equal(out, out2)
 
 
+def _gate_count_random_cases(n=6, seed=20261203):
+    """Seeded shapes on the fused gate-count path: more than 1024 tokens,
+    E <= 512 and K <= 8 (16 lanes a token), the default 64-token tile."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    while len(cases) < n:
+        E = int(rng.choice([8, 16, 40, 64, 96, 128, 200, 256, 384, 512]))
+        K = int(rng.integers(1, min(8, E) + 1))
+        R = int(rng.choice([r for r in (1, 2, 4, 8, 16, 32, 64) if E % r == 0]))
+        N = int(rng.choice([m for m in (1, 2, 4, 8) if R % m == 0]))
+        T = int(rng.integers(1025, 6000))
+        cases.append((T, 64, E, K, R, N))
+    return cases
+
+
+@pytest.mark.parametrize("case", _gate_count_random_cases(),
+                         ids=lambda c: f"T{c[0]}-E{c[2]}-K{c[3]}-R{c[4]}-N{c[5]}")
+def test_fused_gate_count_random(case):
+    T, H, E, K, R, N = case
+    w = mi.Workload("gate_count_rand", T=T, H=H, E=E, K=K, R=R, N=N,
+                    expert="mod8", seed=T)
+    d = mi.make_inputs(w)
+    ref = oracle.dispatch_combine(d["x"], d["logits"], K, R, N,
+                                  d["expert_scale"], w.out_dtype)
+    res = run_fused(w, d)
+    assert res["dev_error"] == 0
+    check_gate(res, ref["topk_idx"], ref["topk_w"])
+    check_layout(res, ref)
+    np.testing.assert_array_equal(res["send"], ref["send"])
+    coef = ref["topk_w"].astype(np.float64) * d["expert_scale"][ref["topk_idx"]]
+    check_out(res["out"], ref["out_exact"],
+              term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef),
+              w.out_dtype)
+
+
 # Batches of up to 1024 tokens (T*K <= 4096) take the one-launch decode
 # step after the gate: ragged and tiny batches, K = 1 and K = E, many nodes,
 # E = 1024, fp32 rows and outputs, no expert scale, no optional outputs.
