@@ -474,6 +474,7 @@ GATE_COUNT_SHAPES = [
     (4133, 32, 512, 8, 128, 16, 64, True, False),
     (1100, 72, 48, 6, 8, 4, 0, False, True),
     (2100, 64, 256, 8, 64, 8, 128, False, True),
+    (2000, 64, 128, 8, 64, 64, 0, False, True),  # 64 nodes: mask bit 63
 ]
 
 
