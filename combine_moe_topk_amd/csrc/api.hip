@@ -22,6 +22,8 @@ int validate(const moe_cfg *c) {
   if (c->E > 4096) return MOE_EINVAL;
   if (c->E % c->R != 0 || c->R % c->N != 0 || c->N > 64) return MOE_EINVAL;
   if ((int64_t)c->T * c->K > INT32_MAX) return MOE_EINVAL;
+  // headroom for int token indexes rounded up to a whole tile (1024)
+  if (c->T > INT32_MAX - 4096) return MOE_EINVAL;
   switch (c->layout_tile) {
     case 0: case 64: case 128: case 256: case 512: case 1024: break;
     default: return MOE_EINVAL;

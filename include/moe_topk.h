@@ -79,7 +79,7 @@ extern "C" {
 
 /* Problem description shared by all calls. */
 typedef struct moe_cfg {
-  int32_t T;           /* tokens, >= 0                                        */
+  int32_t T;           /* tokens, 0..2^31 - 4097; T * K < 2^31              */
   int32_t H;           /* hidden size, >= 1, multiple of 8                    */
   int32_t E;           /* experts, 1..4096                                    */
   int32_t K;           /* experts per token, 1..min(E, 32)                    */

@@ -69,6 +69,8 @@ def cfg(**kw):
     ({"H": 7164}, moe.MOE_EUNSUPPORTED),   # not a multiple of 8
     ({"x_dtype": "f32", "out_dtype": "bf16"}, moe.MOE_OK),
     ({"layout_tile": 1024}, moe.MOE_OK),
+    ({"T": 2**31 - 4097, "K": 1}, moe.MOE_OK),
+    ({"T": 2**31 - 4096, "K": 1}, moe.MOE_EINVAL),  # no tile headroom
 ])
 def test_validate_cfg(kw, code):
     assert moe.moe_validate_cfg(cfg(**kw)) == code
