@@ -134,6 +134,41 @@ def test_gate_selection_paths(E, K, G, per_lane, path):
     check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
 
 
+# Few experts (E from 1 to 16, fewer than the group's lanes, so most lanes
+# hold padding keys), at a one-token, a one-wave-per-token and a 16-lane
+# batch size: ties, signed zeros, few levels, masked experts and the
+# no-renormalisation variant.
+FEW_EK = [(1, 1), (2, 2), (3, 2), (5, 3), (8, 1), (8, 2), (8, 8), (12, 4),
+           (16, 3), (16, 8)]
+FEW_LOGITS = ADV + [
+    ("normal", lambda T, E, K: np.random.Generator(np.random.PCG64(E + K))
+     .standard_normal((T, E), dtype=np.float32)),
+    ("masked", lambda T, E, K: mi.logits_masked(T, E, seed=E + K))]
+
+
+@pytest.mark.parametrize("name,make", FEW_LOGITS,
+                         ids=[a[0] for a in FEW_LOGITS])
+@pytest.mark.parametrize("E,K", FEW_EK, ids=lambda v: str(v))
+@pytest.mark.parametrize("T", [1, 77, 3000])
+def test_gate_few_experts(T, E, K, name, make):
+    lg = make(T, E, K)
+    w = mi.Workload("few", T=T, H=8, E=E, K=K, R=1, N=1)
+    ref_idx, ref_w = oracle.gate(lg, K)
+    idx, wt = gpu_gate(w, lg)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (16, 8), (5, 5)])
+def test_gate_few_experts_no_renorm(E, K):
+    T = 2000
+    lg = np.random.Generator(np.random.PCG64(7)).standard_normal(
+        (T, E), dtype=np.float32)
+    w = mi.Workload("few", T=T, H=8, E=E, K=K, R=1, N=1)
+    ref_idx, ref_w = oracle.gate(lg, K, renorm=False)
+    idx, wt = gpu_gate(w, lg, renorm=False)
+    check_gate({"topk_idx": idx, "topk_w": wt}, ref_idx, ref_w)
+
+
 @pytest.mark.parametrize("T", [300, 2000])  # 64 lanes a token, then 16-32
 @pytest.mark.parametrize("E,K", [(8, 2), (32, 8), (64, 16), (256, 8),
                                  (896, 16), (1000, 32)])
@@ -561,6 +596,25 @@ def test_fused_gate_count_random(case):
     check_out(res["out"], ref["out_exact"],
               term_scale(rows_f64(ref["send"]), ref["slot_pos"], coef),
               w.out_dtype)
+
+
+# Few experts past the decode sizes, through the fused call at several
+# layout tile sizes (64-token tiles take the gate with the count pass).
+FEW_COUNT_SHAPES = [
+    # T, H, E, K, R, N, tile, masked, optional
+    (4096, 64, 8, 2, 8, 1, 0, False, True),      # the Mixtral shape's E, K
+    (1025, 64, 5, 3, 5, 1, 64, False, True),
+    (3333, 32, 16, 8, 4, 2, 256, True, True),
+    (5000, 64, 12, 4, 6, 3, 1024, False, False),
+    (2049, 64, 16, 1, 16, 16, 128, True, True),
+    (4500, 64, 2, 2, 2, 2, 0, False, True),
+]
+
+
+@pytest.mark.parametrize("case", FEW_COUNT_SHAPES,
+                         ids=lambda c: f"T{c[0]}-E{c[2]}-K{c[3]}-tile{c[6]}")
+def test_fused_few_experts(case):
+    test_fused_gate_count(case)
 
 
 # Batches of up to 1024 tokens (T*K <= 4096) take the one-launch decode
