@@ -375,16 +375,24 @@ __device__ void offsets_from_totals(int32_t *ebase, int32_t *nbase, int E,
   __syncthreads();
 }
 
-// With TOTALS the tail row of the table holds each column's total (from
-// the column-parallel scan): every rank workgroup turns the expert and node
-// totals into global exclusive offsets in LDS (workgroup 0 also writes the
-// batch-wide outputs); then it adds its tile's prefixes to get the base of
-// each column.
-// TOTALS false: the tail row already holds the global offsets (the
-// one-workgroup scan wrote them and the batch-wide outputs).
 constexpr int kRankRowRegs = 8;  // table values a thread loads at once
+// Up to this many tiles and columns the rank kernel reads the raw per-tile
+// counts itself (MODE 2) and no scan launch runs.
+constexpr int kFoldTiles = 64;
+constexpr int kFoldCols = 64;
 
-template <int KM, bool TOTALS>
+constexpr int kFoldBatch = 8;  // columns whose loads go out together
+
+// MODE 0: the tail row of the table holds the global offsets (the
+// one-workgroup scan wrote them and the batch-wide outputs).  MODE 1: the
+// tail row holds each column's total (the column-parallel scan): every
+// workgroup turns the expert and node totals into global exclusive offsets
+// in LDS (workgroup 0 also writes the batch-wide outputs), then adds its
+// tile's prefixes.  MODE 2: the table holds the raw per-tile counts (at
+// most kFoldTiles rows of kFoldCols): wave 0, lane r holding tile r, sums
+// every column over all tiles and over the tiles before this one, and the
+// rest is as in MODE 1.
+template <int KM, int MODE>
 __global__ __launch_bounds__(1024) void layout_rank_kernel(
     const int32_t *__restrict__ idx, int T, int K, int E, int R, int N,
     int per_rank, uint32_t m_node, const int32_t *__restrict__ table,
@@ -414,6 +422,43 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   // offsets could start, and as much again for the tile's row); the rest,
   // for very wide tables only, in a loop.
   const int B = blockDim.x;
+  if constexpr (MODE == 2) {
+    __shared__ int32_t ftot[kFoldCols], fpre[kFoldCols];
+    if (threadIdx.x < kWave) {  // wave 0: lane r holds tile r
+      // one inclusive scan over the tiles per column: its last lane is the
+      // column's total, lane b less b's own count this tile's prefix
+      const int b = blockIdx.x;
+      for (int c0 = 0; c0 < cols; c0 += kFoldBatch) {
+        int v[kFoldBatch];
+#pragma unroll
+        for (int u = 0; u < kFoldBatch; ++u)
+          v[u] = lane < (int)gridDim.x && c0 + u < cols
+                     ? table[(size_t)lane * cols + c0 + u]
+                     : 0;
+#pragma unroll
+        for (int u = 0; u < kFoldBatch; ++u) {
+          if (c0 + u < cols) {  // uniform
+            const int inc = wave_inclusive_scan(v[u]);
+            const int all = __builtin_amdgcn_readlane(inc, kWave - 1);
+            const int pre = __builtin_amdgcn_readlane(inc, b) -
+                            __builtin_amdgcn_readlane(v[u], b);
+            if (lane == 0) {
+              ftot[c0 + u] = all;
+              fpre[c0 + u] = pre;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < cr; j += B)
+      ebase[j < E ? j : j + 1] = ftot[j < E ? j : j + R];
+    __syncthreads();
+    offsets_from_totals(ebase, nbase, E, R, N, per_rank, ftot, lo, wsum);
+    for (int j = threadIdx.x; j < cr; j += B)
+      ebase[j < E ? j : j + 1] += fpre[j < E ? j : j + R];
+    __syncthreads();
+  } else {
   int tl[kRankRowRegs], tv[kRankRowRegs];
 #pragma unroll
   for (int u = 0; u < kRankRowRegs; ++u) {
@@ -430,8 +475,8 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   for (int j = kRankRowRegs * B + threadIdx.x; j < cr; j += B)
     ebase[j < E ? j : j + 1] = tail[j < E ? j : j + R];
   __syncthreads();
-  if constexpr (TOTALS) offsets_from_totals(ebase, nbase, E, R, N, per_rank,
-                                            tail, lo, wsum);
+  if constexpr (MODE == 1) offsets_from_totals(ebase, nbase, E, R, N,
+                                               per_rank, tail, lo, wsum);
 #pragma unroll
   for (int u = 0; u < kRankRowRegs; ++u) {
     const int j = u * B + threadIdx.x;
@@ -440,6 +485,7 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
   for (int j = kRankRowRegs * B + threadIdx.x; j < cr; j += B)
     ebase[j < E ? j : j + 1] += tile[j < E ? j : j + R];
   __syncthreads();
+  }
 
   const uint64_t bit = 1ull << lane;
   const uint64_t below = bit - 1;
@@ -693,6 +739,14 @@ hipError_t launch_layout_tail(const moe_cfg &c, const int32_t *topk_idx,
                      lay.rank_off, lay.rank_token_count, lay.node_count,
                      lay.node_off};
   const size_t rank_lds = rank_lds_bytes(c, g.tile_waves);
+  if (g.nblocks >= 1 && g.nblocks <= kFoldTiles && g.cols <= kFoldCols) {
+    // a small table: every rank workgroup sums the raw counts itself
+    hipLaunchKernelGGL((layout_rank_kernel<KM, 2>), dim3(g.nblocks),
+                       dim3(threads), rank_lds, stream, topk_idx, c.T, c.K,
+                       c.E, c.R, c.N, per_rank, m_node, table, lo,
+                       lay.slot_pos, lay.row_src, lay.node_slot);
+    return hipGetLastError();
+  }
   if (g.nblocks <= kSmallTable) {
     // One workgroup scans the few tile rows (rows [0, nblocks) become
     // exclusive prefixes, the tail row the global offsets) and writes the
@@ -705,7 +759,7 @@ hipError_t launch_layout_tail(const moe_cfg &c, const int32_t *topk_idx,
                        lay.node_off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || g.nblocks == 0) return e;
-    hipLaunchKernelGGL((layout_rank_kernel<KM, false>), dim3(g.nblocks),
+    hipLaunchKernelGGL((layout_rank_kernel<KM, 0>), dim3(g.nblocks),
                        dim3(threads), rank_lds, stream, topk_idx, c.T, c.K,
                        c.E, c.R, c.N, per_rank, m_node, table, lo,
                        lay.slot_pos, lay.row_src, lay.node_slot);
@@ -720,7 +774,7 @@ hipError_t launch_layout_tail(const moe_cfg &c, const int32_t *topk_idx,
                      g.nblocks, g.cols);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((layout_rank_kernel<KM, true>), dim3(g.nblocks),
+  hipLaunchKernelGGL((layout_rank_kernel<KM, 1>), dim3(g.nblocks),
                      dim3(threads), rank_lds, stream, topk_idx, c.T, c.K, c.E,
                      c.R, c.N, per_rank, m_node, table, lo, lay.slot_pos,
                      lay.row_src, lay.node_slot);
