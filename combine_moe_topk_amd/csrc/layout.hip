@@ -27,7 +27,9 @@
 //   scan : the count table to per-tile exclusive prefixes and column totals
 //          (one workgroup up to 32 tiles, which also writes the offsets;
 //          else column-parallel, and the rank workgroups derive the
-//          offsets from the totals)
+//          offsets from the totals); none for a small table (up to 64
+//          tiles of 64 columns), whose raw counts every rank workgroup
+//          sums itself
 //   rank : rebuilds the tile bitmaps and writes slot_pos, row_src, node_slot
 // In the fused call the gate can write the counts itself (gate.hip), and
 // only scan and rank run here.  The count table lives in the caller's
