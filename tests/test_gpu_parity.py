@@ -475,6 +475,10 @@ def test_empty_input():
     (129, 264, 64, 32, 64, 64, mi.BF16, mi.BF16),  # K = 32, N = 64
     (300, 64, 4096, 8, 64, 8, mi.BF16, mi.BF16),  # E = 4096: 64-token tiles
     (40, 16384, 16, 4, 4, 2, mi.BF16, mi.F32),  # H = 16384: 2048 units
+    # past the decode sizes: E = 4096 (64 keys a lane, one-wave layout
+    # tiles, the rank kernel's loop over a wide table) and K = 32, N = 64
+    (3000, 64, 4096, 8, 64, 8, mi.BF16, mi.BF16),
+    (2000, 64, 64, 32, 64, 64, mi.BF16, mi.F32),
 ])
 def test_fused_edge_shapes(T, H, E, K, R, N, xdt, odt):
     w = mi.Workload("edge", T=T, H=H, E=E, K=K, R=R, N=N, x_dtype=xdt,
