@@ -12,8 +12,6 @@ constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-int elem_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : 2; }
-
 int validate(const moe_cfg *c) {
   if (!c) return MOE_EINVAL;
   if (c->T < 0 || c->H < 1 || c->E < 1 || c->K < 1 || c->R < 1 || c->N < 1)

@@ -34,7 +34,7 @@ namespace {
 // its node's per_node flags, and a ballot of the non-empty lanes is the
 // expert's node mask.
 __global__ __launch_bounds__(256) void expert_tables_kernel(
-    const uint8_t *__restrict__ holds, int E, int G, int N, int per_node,
+    const uint8_t *__restrict__ holds, int E, int N, int per_node,
     uint64_t *__restrict__ nodes, uint64_t *__restrict__ rank_bits) {
   const int lane = threadIdx.x % kWave;
   const int e = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
@@ -250,7 +250,7 @@ hipError_t launch_assign(const moe_cfg &c, const int32_t *topk_idx,
   uint64_t *rbits = enodes + c.E;
   const int per_node = c.R / c.N;
   hipLaunchKernelGGL(expert_tables_kernel, dim3((c.E + 3) / 4), dim3(256), 0,
-                     stream, holds, c.E, c.R, c.N, per_node, enodes, rbits);
+                     stream, holds, c.E, c.N, per_node, enodes, rbits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.T == 0) return e;
   const dim3 grid((c.T + 3) / 4), block(256);  // one wave per token

@@ -26,7 +26,8 @@ __global__ __launch_bounds__(256) void gate_kernel(
   // every lane of a wave runs the DPP reductions (whole waves leave only
   // when the wave's first token is past the end)
   const bool live = t < T;
-  if (blockIdx.x * kTokensPerBlock + (threadIdx.x & ~63) / G >= T) return;
+  if ((int)blockIdx.x * kTokensPerBlock + (int)(threadIdx.x & ~63u) / G >= T)
+    return;
   if (!live) t = T - 1;
   float v[C];
   gate::load_keys<G, C, FULL>(logits + (size_t)t * E, sub, E, v);
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(1024) void gate_count_kernel(
     const int base = t0 + i * 64;
     // waves whose tokens are all past the end skip the pass (wave-uniform:
     // the selection synchronises only within the wave)
-    if (base + (threadIdx.x & ~63) / G >= T) continue;
+    if (base + (int)(threadIdx.x & ~63u) / G >= T) continue;
     int t = base + j;
     const bool live = t < T;
     if (!live) t = T - 1;

@@ -231,8 +231,9 @@ __global__ __launch_bounds__(1024) void layout_scan_cols_kernel(
   __shared__ int32_t part[kScanChunks][kScanCols];
   const int cl = threadIdx.x % kScanCols;
   const int ch = threadIdx.x / kScanCols;
-  const int c = min(blockIdx.x * kScanCols + cl, cols - 1);
-  const bool col_ok = blockIdx.x * kScanCols + cl < cols;
+  const int c0 = (int)blockIdx.x * kScanCols + cl;
+  const int c = min(c0, cols - 1);
+  const bool col_ok = c0 < cols;
   const int per = (nblocks + kScanChunks - 1) / kScanChunks;
   const int r0 = min(nblocks, ch * per);
   const int r1 = min(nblocks, r0 + per);
